@@ -1,0 +1,148 @@
+"""CPU reference checker (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product path (``block_sparse_attention_mask_amd``)
+never imports it.  The arithmetic lives in ``oracle.c`` (plain C, fp64,
+OpenMP); this module only builds it with gcc and marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, -O2)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        L.oracle_build_csr.restype = I64
+        L.oracle_build_csr.argtypes = [P, P, ctypes.c_float, P, I64, I64, I64, ctypes.c_int,
+                                       P, P, P, I64]
+        L.oracle_perm_from_labels.restype = ctypes.c_int
+        L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
+        L.oracle_schedule.restype = ctypes.c_int
+        L.oracle_schedule.argtypes = [P, I64, I64, I64, I64, I64, I64, P]
+        L.oracle_attn_rows.restype = ctypes.c_int
+        L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
+                                       P, P, P, P, P, ctypes.c_int, ctypes.c_double,
+                                       I64, P, P, P]
+        L.oracle_count_pairs.restype = I64
+        L.oracle_count_pairs.argtypes = [P, P, I64, I64, I64, ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def build_csr(mask=None, T=None, p: float = 0.0, lw_map=None, nQB: int = 0, force_diag: bool = True,
+              want_lw: bool = False):
+    """Returns (row_ptr int32[R+1], col int32[nnz], lw float32[nnz] or None)."""
+    src = mask if mask is not None else T
+    R, nKB = src.shape
+    mask = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    T = None if T is None else np.ascontiguousarray(T, dtype=np.float32)
+    lw_map = None if lw_map is None else np.ascontiguousarray(lw_map, dtype=np.float32)
+    row_ptr = np.zeros(R + 1, dtype=np.int32)
+    n = lib().oracle_build_csr(_p(mask), _p(T), float(p), _p(lw_map), R, nQB or nKB, nKB,
+                               int(force_diag), _p(row_ptr), None, None, 0)
+    if n < 0:
+        raise ValueError("oracle_build_csr failed: %d" % n)
+    col = np.zeros(max(n, 1), dtype=np.int32)
+    lw = np.zeros(max(n, 1), dtype=np.float32) if (want_lw or lw_map is not None) else None
+    n2 = lib().oracle_build_csr(_p(mask), _p(T), float(p), _p(lw_map), R, nQB or nKB, nKB,
+                                int(force_diag), _p(row_ptr), _p(col), _p(lw), n)
+    assert n2 == n
+    return row_ptr, col[:n], (None if lw is None else lw[:n])
+
+
+def perm_from_labels(labels: np.ndarray, n_clusters: int) -> np.ndarray:
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    BH, N = labels.shape
+    perm = np.empty((BH, N), dtype=np.int32)
+    rc = lib().oracle_perm_from_labels(_p(labels), BH, N, int(n_clusters), _p(perm))
+    if rc:
+        raise ValueError("oracle_perm_from_labels failed: %d" % rc)
+    return perm
+
+
+def schedule(row_ptr: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int, n_xcd: int = 1):
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    order = np.empty(B * Hq * nQB, dtype=np.int32)
+    rc = lib().oracle_schedule(_p(row_ptr), B, Hq, Hkv, nQB, W, n_xcd, _p(order))
+    if rc:
+        raise ValueError("oracle_schedule failed: %d" % rc)
+    return order
+
+
+def attn_rows(q, k, v, row_ptr, col, lw, block: int, rows: np.ndarray, perm_q=None, perm_k=None,
+              causal: bool = False, scale: Optional[float] = None):
+    """q [B][Hq][N][d], k/v [B][Hkv][N][d] as uint16 bf16 bits (any strides with
+    a contiguous last dimension).  rows: flat (b*Hq + h)*N + t, original t.
+    Returns (O float64 [n][d], LSE float64 [n])."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    for a in (q, k, v):
+        assert a.dtype == np.uint16 and a.strides[-1] == 2
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    st = lambda a: np.array([s // 2 for s in a.strides[:3]], dtype=np.int64)
+    qs, ks, vs = st(q), st(k), st(v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), d), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    lw = None if lw is None else np.ascontiguousarray(lw, dtype=np.float32)
+    perm_q = None if perm_q is None else np.ascontiguousarray(perm_q, dtype=np.int32)
+    perm_k = None if perm_k is None else np.ascontiguousarray(perm_k, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rc = lib().oracle_attn_rows(_p(q), _p(k), _p(v), _p(qs), _p(ks), _p(vs), B, Hq, Hkv, N, d, block,
+                                _p(row_ptr), _p(col), _p(lw), _p(perm_q), _p(perm_k), int(causal),
+                                float(scale), len(rows), _p(rows), _p(out), _p(lse))
+    if rc:
+        raise ValueError("oracle_attn_rows failed: %d" % rc)
+    return out, lse
+
+
+def count_pairs(row_ptr, col, N: int, block: int, causal: bool) -> int:
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    n = lib().oracle_count_pairs(_p(row_ptr), _p(col), len(row_ptr) - 1, N, block, int(causal))
+    if n < 0:
+        raise ValueError("oracle_count_pairs failed")
+    return int(n)
+
+
+def attn_full(w, row_ptr, col, lw, perm_q=None, perm_k=None, rows=None):
+    """Convenience: every row (or the given rows) of workload ``w``."""
+    if rows is None:
+        rows = np.arange(w.B * w.Hq * w.N, dtype=np.int64)
+    return attn_rows(w.q, w.k, w.v, row_ptr, col, lw, w.block, rows, perm_q, perm_k, w.causal)

@@ -1,0 +1,305 @@
+/*
+ * CPU reference checker for block-sparse attention (test infrastructure).
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg use
+ * this file.  It shares no code with the GPU library: plain C, fp64
+ * arithmetic, OpenMP across independent rows, no blocking or fusion.
+ *
+ * What each routine computes and where the pages define it:
+ *
+ *  oracle_build_csr   Block mask -> per-row ascending KV-block lists.  A row is
+ *                     one (batch, query head, query block); an entry is kept
+ *                     when mask != 0, or when the threshold T <= p
+ *                     (ScalingAttention, section 5.2, Eq. 2: M_p = I(T <= p)),
+ *                     or when it is the row's diagonal block (always kept).
+ *                     The ascending order is the order in which the CRM
+ *                     forward iterator of ScalingAttention (section 7.3,
+ *                     Algorithm 2) walks the active KV blocks.  Log-weights
+ *                     are copied bit for bit from the log-weight map.
+ *  oracle_perm_from_labels
+ *                     Gather permutation that makes every cluster contiguous
+ *                     (InstaGen, section 4: tokens permuted into contiguous
+ *                     blocks by cluster); ties keep the original order.
+ *  oracle_schedule    Query-row order: KV-group-major over heads
+ *                     (WaveAlign, section VI-B: sequential-head scheduling),
+ *                     consecutive buckets of at most W rows each sorted by
+ *                     descending nonzero-block count (WaveAlign, section IV-D,
+ *                     NNZ-guided intra-wave alignment), then the launch-index
+ *                     remap that gives each XCD a contiguous run.
+ *  oracle_attn_rows   Dense-masked softmax attention, InstaGen section 3.1
+ *                     Eq. (1)-(3), with the per-block log-weight added to the
+ *                     scaled logit (InstaGen Algorithm 1, Horvitz-Thompson
+ *                     weights as log w).  Masked pairs are -inf.
+ *  oracle_count_pairs Number of allowed (query, key) token pairs; the FLOP
+ *                     convention of 4*d per pair is the one behind INTRA's
+ *                     GFLOPS column (INTRA, Table 1 and the overhead table).
+ *
+ * Every function is pinned by the CPU test suite against something other
+ * than itself (library routines, brute force, closed forms, invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_ERR_ARG (-1)
+#define OR_ERR_CAPACITY (-3)
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* mask -> CSR                                                               */
+/* ------------------------------------------------------------------------ */
+static int kept(const uint8_t *mask, const float *T, float p, int64_t r, int64_t v,
+                int64_t nQB, int64_t nKB, int force_diag) {
+  int64_t i = r * nKB + v;
+  int k;
+  if (mask)
+    k = mask[i] != 0;
+  else
+    k = T[i] <= p; /* NaN compares false */
+  if (force_diag && v == r % nQB) k = 1;
+  return k;
+}
+
+/* Fills row_ptr[R+1]; when col != NULL also col (and lw when lw != NULL).
+ * Returns nnz, or a negative error. */
+int64_t oracle_build_csr(const uint8_t *mask, const float *T, float p, const float *lw_map,
+                         int64_t R, int64_t nQB, int64_t nKB, int force_diag, int32_t *row_ptr,
+                         int32_t *col, float *lw, int64_t capacity) {
+  if ((!mask && !T) || R < 0 || nQB <= 0 || nKB <= 0 || !row_ptr) return OR_ERR_ARG;
+  int64_t n = 0;
+  row_ptr[0] = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t v = 0; v < nKB; ++v) {
+      if (!kept(mask, T, p, r, v, nQB, nKB, force_diag)) continue;
+      if (col) {
+        if (n >= capacity) return OR_ERR_CAPACITY;
+        col[n] = (int32_t)v;
+        if (lw) {
+          if (lw_map)
+            memcpy(&lw[n], &lw_map[r * nKB + v], sizeof(float));
+          else
+            lw[n] = 0.0f;
+        }
+      }
+      ++n;
+    }
+    row_ptr[r + 1] = (int32_t)n;
+  }
+  return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* labels -> permutation                                                     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t key;
+  int32_t idx;
+} key_idx;
+
+static int cmp_key_idx(const void *a, const void *b) {
+  const key_idx *x = (const key_idx *)a, *y = (const key_idx *)b;
+  if (x->key != y->key) return x->key < y->key ? -1 : 1;
+  return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+/* perm[bh][i] = original index of the token at permuted position i, sorted by
+ * (label, original index).  Labels outside [0, n_clusters) sort after every
+ * valid label. */
+int oracle_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_t n_clusters,
+                            int32_t *perm) {
+  if (!labels || !perm || BH < 0 || N < 0 || n_clusters <= 0) return OR_ERR_ARG;
+  key_idx *buf = (key_idx *)malloc(sizeof(key_idx) * (size_t)(N > 0 ? N : 1));
+  if (!buf) return OR_ERR_ARG;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    for (int64_t i = 0; i < N; ++i) {
+      int32_t l = labels[bh * N + i];
+      buf[i].key = (l >= 0 && l < n_clusters) ? l : n_clusters;
+      buf[i].idx = (int32_t)i;
+    }
+    qsort(buf, (size_t)N, sizeof(key_idx), cmp_key_idx);
+    for (int64_t i = 0; i < N; ++i) perm[bh * N + i] = buf[i].idx;
+  }
+  free(buf);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* row schedule                                                              */
+/* ------------------------------------------------------------------------ */
+/* Logical sequence: for each batch b and KV head g, the rows of the G = Hq/Hkv
+ * query heads that share g, query block u outer and head inner.  Buckets of
+ * at most W consecutive entries within one (b, g) segment are sorted by
+ * (nnz descending, sequence position ascending).  With n_xcd > 1 the list is
+ * then dealt so that launch index i runs logical position start(i % n_xcd) +
+ * i / n_xcd, where XCD x receives the x-th contiguous slice. */
+int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t nQB,
+                    int64_t W, int64_t n_xcd, int32_t *order) {
+  if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W <= 0)
+    return OR_ERR_ARG;
+  int64_t G = Hq / Hkv, R = B * Hq * nQB, seg = G * nQB;
+  int32_t *logical = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  key_idx *buf = (key_idx *)malloc(sizeof(key_idx) * (size_t)W);
+  if (!logical || !buf) return OR_ERR_ARG;
+  int64_t pos = 0;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t g = 0; g < Hkv; ++g)
+      for (int64_t u = 0; u < nQB; ++u)
+        for (int64_t j = 0; j < G; ++j) logical[pos++] = (int32_t)((b * Hq + g * G + j) * nQB + u);
+  for (int64_t s0 = 0; s0 < R; s0 += seg) {
+    for (int64_t b0 = s0; b0 < s0 + seg; b0 += W) {
+      int64_t n = (b0 + W <= s0 + seg) ? W : s0 + seg - b0;
+      for (int64_t i = 0; i < n; ++i) {
+        int32_t r = logical[b0 + i];
+        buf[i].key = -(int64_t)(row_ptr[r + 1] - row_ptr[r]);
+        buf[i].idx = (int32_t)i;
+      }
+      qsort(buf, (size_t)n, sizeof(key_idx), cmp_key_idx);
+      int32_t tmp[4096];
+      int32_t *t = n <= 4096 ? tmp : (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+      for (int64_t i = 0; i < n; ++i) t[i] = logical[b0 + buf[i].idx];
+      memcpy(&logical[b0], t, sizeof(int32_t) * (size_t)n);
+      if (t != tmp) free(t);
+    }
+  }
+  if (n_xcd <= 1) {
+    memcpy(order, logical, sizeof(int32_t) * (size_t)R);
+  } else {
+    for (int64_t i = 0; i < R; ++i) {
+      int64_t x = i % n_xcd, k = i / n_xcd, start = 0;
+      for (int64_t y = 0; y < x; ++y) start += (R - 1 - y) / n_xcd + 1; /* launches on XCD y */
+      order[i] = logical[start + k];
+    }
+  }
+  free(buf);
+  free(logical);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* attention                                                                 */
+/* ------------------------------------------------------------------------ */
+/* rows[i] = (b * Hq + h) * N + t with t an original (unpermuted) token index.
+ * Strides are in elements for (batch, head, token); the head dimension is
+ * contiguous.  perm_q is [B*Hq][N], perm_k is [B*Hkv][N] (gather form: the
+ * original index at each permuted position) or NULL for the identity.
+ * out[i*d .. i*d+d-1] and lse[i] receive O and ln(sum exp) of that row; a row
+ * with no allowed key gets O = 0 and LSE = -inf. */
+int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const int64_t *q_str, const int64_t *k_str, const int64_t *v_str, int64_t B,
+                     int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t block,
+                     const int32_t *row_ptr, const int32_t *col, const float *lw,
+                     const int32_t *perm_q, const int32_t *perm_k, int causal, double scale,
+                     int64_t n_rows, const int64_t *rows, double *out, double *lse) {
+  if (!q || !k || !v || !row_ptr || !col || !rows || !out || B <= 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv || N <= 0 || d <= 0 || block <= 0)
+    return OR_ERR_ARG;
+  int64_t G = Hq / Hkv, nQB = (N + block - 1) / block, nKB = nQB;
+  /* permuted position of every original token */
+  int32_t *pos_q = NULL, *pos_k = NULL;
+  if (perm_q) {
+    pos_q = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B * Hq * N));
+    for (int64_t bh = 0; bh < B * Hq; ++bh)
+      for (int64_t i = 0; i < N; ++i) pos_q[bh * N + perm_q[bh * N + i]] = (int32_t)i;
+  }
+  if (perm_k) {
+    pos_k = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B * Hkv * N));
+    for (int64_t bh = 0; bh < B * Hkv; ++bh)
+      for (int64_t i = 0; i < N; ++i) pos_k[bh * N + perm_k[bh * N + i]] = (int32_t)i;
+  }
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *x = (double *)malloc(sizeof(double) * (size_t)N);
+    char *allowed = (char *)malloc((size_t)N);
+    char *present = (char *)malloc((size_t)nKB);
+    double *bias = (double *)malloc(sizeof(double) * (size_t)nKB);
+    double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      int64_t flat = rows[i];
+      int64_t bh = flat / N, t = flat % N;
+      if (bh < 0 || bh >= B * Hq) {
+        bad = 1;
+        continue;
+      }
+      int64_t b = bh / Hq, h = bh % Hq, g = h / G, bg = b * Hkv + g;
+      int64_t pq = pos_q ? pos_q[bh * N + t] : t;
+      int64_t u = pq / block;
+      int64_t r = bh * nQB + u;
+      memset(present, 0, (size_t)nKB);
+      for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+        present[col[e]] = 1;
+        bias[col[e]] = lw ? (double)lw[e] : 0.0;
+      }
+      const uint16_t *qrow = q + b * q_str[0] + h * q_str[1] + t * q_str[2];
+      for (int64_t c = 0; c < d; ++c) qv[c] = bf16_to_double(qrow[c]);
+      double m = -INFINITY;
+      for (int64_t s = 0; s < N; ++s) {
+        int64_t ps = pos_k ? pos_k[bg * N + s] : s;
+        int64_t vb = ps / block;
+        allowed[s] = present[vb] && !(causal && s > t);
+        if (!allowed[s]) continue;
+        const uint16_t *krow = k + b * k_str[0] + g * k_str[1] + s * k_str[2];
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qv[c] * bf16_to_double(krow[c]);
+        x[s] = scale * dot + bias[vb];
+        if (x[s] > m) m = x[s];
+      }
+      for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+      double Z = 0.0;
+      if (m != -INFINITY) {
+        for (int64_t s = 0; s < N; ++s) {
+          if (!allowed[s]) continue;
+          double w = exp(x[s] - m);
+          Z += w;
+          const uint16_t *vrow = v + b * v_str[0] + g * v_str[1] + s * v_str[2];
+          for (int64_t c = 0; c < d; ++c) acc[c] += w * bf16_to_double(vrow[c]);
+        }
+      }
+      for (int64_t c = 0; c < d; ++c) out[i * d + c] = Z > 0.0 ? acc[c] / Z : 0.0;
+      if (lse) lse[i] = Z > 0.0 ? m + log(Z) : -INFINITY;
+    }
+    free(x);
+    free(allowed);
+    free(present);
+    free(bias);
+    free(qv);
+    free(acc);
+  }
+  free(pos_q);
+  free(pos_k);
+  return bad ? OR_ERR_ARG : OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* allowed-pair count                                                        */
+/* ------------------------------------------------------------------------ */
+/* Counts (query token, key token) pairs that take part: both real (index <
+ * N), the key block listed for the query's block row, and s <= t when causal
+ * (positions are the unpermuted ones; causal is only defined without a
+ * permutation). Token-by-token loop. */
+int64_t oracle_count_pairs(const int32_t *row_ptr, const int32_t *col, int64_t R, int64_t N,
+                           int64_t block, int causal) {
+  if (!row_ptr || !col || R < 0 || N <= 0 || block <= 0) return OR_ERR_ARG;
+  int64_t nQB = (N + block - 1) / block, total = 0;
+#pragma omp parallel for reduction(+ : total) schedule(dynamic, 8)
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t u = r % nQB;
+    for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+      int64_t vb = col[e];
+      for (int64_t t = u * block; t < (u + 1) * block && t < N; ++t)
+        for (int64_t s = vb * block; s < (vb + 1) * block && s < N; ++s)
+          if (!causal || s <= t) ++total;
+    }
+  }
+  return total;
+}
