@@ -1,0 +1,11 @@
+"""Block-sparse (optionally permuted) softmax attention forward on MI355X.
+
+The compute path is the HIP library ``libbsattn.so`` (C ABI in
+``include/bsattn.h``); this package holds its thin Python binding
+(``api``), the composition of one pass of the path (``pipeline``), the
+seeded input generators (``synth``) and the pair/FLOP accounting
+(``metrics``).
+"""
+from ._lib import BsaError, EXPORTS, LIB_PATH  # noqa: F401
+from .api import (attn_fwd, build_csr, csr_count, csr_fill, device_cus, perm_from_labels,  # noqa: F401
+                  permute_rows, schedule, unpermute_rows, version)

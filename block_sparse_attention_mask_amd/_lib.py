@@ -1,0 +1,86 @@
+"""ctypes declarations for libbsattn.so (the C ABI in include/bsattn.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbsattn.so")
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+I64 = ctypes.c_int64
+I64x3 = ctypes.c_int64 * 3
+
+BSA_OK = 0
+BSA_ERR_ARG = -1
+BSA_ERR_UNSUPPORTED = -2
+BSA_ERR_CAPACITY = -3
+BSA_ERR_HIP = -4
+
+# Every symbol include/bsattn.h declares.
+EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_perm_from_labels",
+           "bsa_permute_rows", "bsa_unpermute_rows", "bsa_schedule", "bsa_attn_fwd",
+           "bsa_device_cus")
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", P), ("k", P), ("v", P), ("o", P), ("lse", P),
+        ("B", I32), ("Hq", I32), ("Hkv", I32), ("d", I32), ("block", I32),
+        ("N", I64),
+        ("q_str", I64x3), ("k_str", I64x3), ("v_str", I64x3), ("o_str", I64x3),
+        ("row_ptr", P), ("col", P), ("lw", P), ("order", P),
+        ("n_order", I64),
+        ("scatter_perm_q", P),
+        ("scale", ctypes.c_float),
+        ("causal", I32),
+    ]
+
+
+_lib = None
+
+
+class BsaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        msg = load().bsa_strerror(code).decode() if _lib is not None else str(code)
+        super().__init__("%s failed: %s (%d)" % (fn, msg, code))
+        self.code = code
+
+
+def load():
+    """Load the in-tree HIP library; there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libbsattn.so is not built (run __graft_entry__.build() or "
+                               "python block_sparse_attention_mask_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bsa_version.restype = ctypes.c_int
+        L.bsa_version.argtypes = []
+        L.bsa_strerror.restype = ctypes.c_char_p
+        L.bsa_strerror.argtypes = [ctypes.c_int]
+        L.bsa_csr_count.restype = ctypes.c_int
+        L.bsa_csr_count.argtypes = [P, P, ctypes.c_float, I64, I32, I32, ctypes.c_int, P,
+                                    ctypes.POINTER(I64), P]
+        L.bsa_csr_fill.restype = ctypes.c_int
+        L.bsa_csr_fill.argtypes = [P, P, ctypes.c_float, P, I64, I32, I32, ctypes.c_int, P, P, P,
+                                   I64, P]
+        L.bsa_perm_from_labels.restype = ctypes.c_int
+        L.bsa_perm_from_labels.argtypes = [P, I64, I64, I32, P, P]
+        for fn in (L.bsa_permute_rows, L.bsa_unpermute_rows):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P]
+        L.bsa_schedule.restype = ctypes.c_int
+        L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P]
+        L.bsa_attn_fwd.restype = ctypes.c_int
+        L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
+        L.bsa_device_cus.restype = ctypes.c_int
+        L.bsa_device_cus.argtypes = []
+        _lib = L
+    return _lib
+
+
+def check(fn: str, rc: int) -> None:
+    if rc != BSA_OK:
+        raise BsaError(fn, rc)

@@ -1,0 +1,175 @@
+"""Python binding of libbsattn.so.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory (tensors) and the stream
+(``torch.cuda.current_stream()``).  bf16 tensors may be ``torch.bfloat16`` or
+``torch.uint16``/``int16`` holding bf16 bit patterns; the head dimension must
+be contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import AttnArgs, I64, I64x3, check, load
+
+__all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
+           "unpermute_rows", "schedule", "attn_fwd", "device_cus"]
+
+_BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s has dtype %s" % (name, t.dtype))
+    return t
+
+
+def _strides(t: torch.Tensor) -> I64x3:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B][H][N][d] tensor with contiguous last dimension")
+    return I64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def version() -> int:
+    return load().bsa_version()
+
+
+def device_cus() -> int:
+    n = load().bsa_device_cus()
+    if n < 0:
+        check("bsa_device_cus", n)
+    return n
+
+
+def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,
+              row_ptr: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, int]:
+    src = mask if mask is not None else T
+    R, nKB = src.shape
+    nQB = nKB if nQB is None else nQB
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+    if T is not None:
+        _dev(T, "T", torch.float32)
+    if not src.is_contiguous():
+        raise ValueError("mask / T must be contiguous [R][nKB]")
+    if row_ptr is None:
+        row_ptr = torch.empty(R + 1, dtype=torch.int32, device=src.device)
+    nnz = I64(0)
+    check("bsa_csr_count", load().bsa_csr_count(_ptr(mask), _ptr(T), float(p), R, nQB, nKB,
+                                                int(force_diag), _ptr(row_ptr), ctypes.byref(nnz),
+                                                _stream(stream)))
+    return row_ptr, int(nnz.value)
+
+
+def csr_fill(row_ptr: torch.Tensor, nnz: int, mask=None, T=None, p: float = 0.0, lw_map=None,
+             nQB: Optional[int] = None, force_diag: bool = True, want_lw: bool = False,
+             col=None, lw=None, stream=None):
+    src = mask if mask is not None else T
+    R, nKB = src.shape
+    nQB = nKB if nQB is None else nQB
+    dev = src.device
+    if col is None:
+        col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    if lw is None and (want_lw or lw_map is not None):
+        lw = torch.empty(max(nnz, 1), dtype=torch.float32, device=dev)
+    if lw_map is not None:
+        _dev(lw_map, "lw_map", torch.float32)
+    check("bsa_csr_fill", load().bsa_csr_fill(_ptr(mask), _ptr(T), float(p), _ptr(lw_map), R, nQB, nKB,
+                                              int(force_diag), _ptr(row_ptr), _ptr(col), _ptr(lw),
+                                              col.numel(), _stream(stream)))
+    return col[:nnz], (None if lw is None else lw[:nnz])
+
+
+def build_csr(mask=None, T=None, p: float = 0.0, lw_map=None, nQB: Optional[int] = None,
+              force_diag: bool = True, want_lw: bool = False, stream=None):
+    """bsa_csr_count + allocation + bsa_csr_fill -> (row_ptr, col, lw or None)."""
+    row_ptr, nnz = csr_count(mask, T, p, nQB, force_diag, stream=stream)
+    col, lw = csr_fill(row_ptr, nnz, mask, T, p, lw_map, nQB, force_diag, want_lw, stream=stream)
+    return row_ptr, col, lw
+
+
+def perm_from_labels(labels: torch.Tensor, n_clusters: int, perm=None, stream=None) -> torch.Tensor:
+    _dev(labels, "labels", torch.int32)
+    labels = labels.contiguous()
+    BH, N = labels.shape
+    if perm is None:
+        perm = torch.empty_like(labels)
+    check("bsa_perm_from_labels", load().bsa_perm_from_labels(_ptr(labels), BH, N, int(n_clusters),
+                                                              _ptr(perm), _stream(stream)))
+    return perm
+
+
+def _permute(fn_name: str, src: torch.Tensor, perm: torch.Tensor, dst=None, stream=None):
+    _dev(src, "src", _BF16_LIKE)
+    _dev(perm, "perm", torch.int32)
+    B, H, N, d = src.shape
+    if dst is None:
+        dst = torch.empty_like(src, memory_format=torch.contiguous_format)
+    fn = getattr(load(), fn_name)
+    check(fn_name, fn(_ptr(src), _ptr(dst), _ptr(perm.contiguous()), B, H, N, d, _strides(src),
+                      _strides(dst), _stream(stream)))
+    return dst
+
+
+def permute_rows(src, perm, dst=None, stream=None):
+    """dst[b][h][i] = src[b][h][perm[b*H + h][i]]."""
+    return _permute("bsa_permute_rows", src, perm, dst, stream)
+
+
+def unpermute_rows(src, perm, dst=None, stream=None):
+    """dst[b][h][perm[b*H + h][i]] = src[b][h][i]."""
+    return _permute("bsa_unpermute_rows", src, perm, dst, stream)
+
+
+def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_rows: int = 0,
+             n_xcd: int = 8, order=None, stream=None) -> torch.Tensor:
+    _dev(row_ptr, "row_ptr", torch.int32)
+    if order is None:
+        order = torch.empty(B * Hq * nQB, dtype=torch.int32, device=row_ptr.device)
+    check("bsa_schedule", load().bsa_schedule(_ptr(row_ptr), B, Hq, Hkv, nQB, int(wave_rows), int(n_xcd),
+                                              _ptr(order), _stream(stream)))
+    return order
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+             col: torch.Tensor, block: int, lw: Optional[torch.Tensor] = None,
+             order: Optional[torch.Tensor] = None, scatter_perm_q: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             want_lse: bool = False, scale: float = 0.0, causal: bool = False, stream=None):
+    """Block-sparse attention forward; returns (out, lse or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, _BF16_LIKE)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B * Hq, N), dtype=torch.float32, device=q.device)
+    a = AttnArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.B, a.Hq, a.Hkv, a.d, a.block, a.N = B, Hq, Hkv, d, int(block), N
+    a.q_str, a.k_str, a.v_str, a.o_str = _strides(q), _strides(k), _strides(v), _strides(out)
+    a.row_ptr, a.col = _ptr(row_ptr), _ptr(col)
+    a.lw = _ptr(lw)
+    a.order = _ptr(order)
+    a.n_order = 0 if order is None else order.numel()
+    a.scatter_perm_q = _ptr(scatter_perm_q)
+    a.scale = float(scale)
+    a.causal = int(bool(causal))
+    check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out, lse

@@ -1,0 +1,168 @@
+// Cluster labels -> gather permutation, and row gather / scatter of bf16
+// token-major tensors.
+//
+// Permuted block-sparse attention lays every cluster out contiguously before
+// the block-sparse kernel (InstaGen, section 4) and restores the output order
+// afterwards (WaveAlign, section V: permute query rows, restore outputs).
+//
+// perm_from_labels is a stable counting sort by (label, original index): one
+// workgroup per (batch, head); each of its four wavefronts owns a contiguous
+// quarter of the tokens.  Pass 1 histograms labels per quarter in LDS, a scan
+// turns the histograms into per-(quarter, label) write cursors, pass 2 walks
+// each quarter in token order 64 tokens at a time: lanes with equal labels
+// find each other with one ballot per label bit, take their rank among the
+// lower lanes, and the lowest of them advances the cursor.
+#include "bsa_internal.h"
+
+namespace {
+
+constexpr int kPermWaves = 4;
+constexpr int kMaxClusters = 4095;  // + 1 overflow bucket for out-of-range labels
+
+__global__ __launch_bounds__(256) void perm_from_labels_kernel(const int32_t *__restrict__ labels,
+                                                               int64_t N, int C,
+                                                               int32_t *__restrict__ perm) {
+  __shared__ int32_t cur[kPermWaves][kMaxClusters + 1];
+  __shared__ int32_t tot[256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t bh = blockIdx.x;
+  const int32_t *lab = labels + bh * N;
+  int32_t *out = perm + bh * N;
+  const int nb = C + 1;  // buckets; bucket C collects out-of-range labels
+  for (int i = tid; i < kPermWaves * nb; i += 256) cur[i / nb][i % nb] = 0;
+  __syncthreads();
+  const int64_t seg = (N + kPermWaves - 1) / kPermWaves;
+  const int64_t s0 = wave * seg;
+  const int64_t s1 = s0 + seg < N ? s0 + seg : N;
+  for (int64_t t = s0 + lane; t < s1; t += 64) {
+    int32_t l = lab[t];
+    if (l < 0 || l >= C) l = C;
+    atomicAdd(&cur[wave][l], 1);
+  }
+  __syncthreads();
+  // exclusive scan in bucket-major, quarter-minor order
+  const int per = (nb + 255) / 256;
+  const int b0 = tid * per, b1 = b0 + per < nb ? b0 + per : nb;
+  int32_t s = 0;
+  for (int bk = b0; bk < b1; ++bk)
+    for (int w = 0; w < kPermWaves; ++w) s += cur[w][bk];
+  tot[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 256; ++i) {
+      int32_t x = tot[i];
+      tot[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  int32_t run = tot[tid];
+  for (int bk = b0; bk < b1; ++bk)
+    for (int w = 0; w < kPermWaves; ++w) {
+      int32_t x = cur[w][bk];
+      cur[w][bk] = run;
+      run += x;
+    }
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < nb) ++nbits;
+  const uint64_t below = bsa_lanemask_lt(lane);
+  for (int64_t c0 = s0; c0 < s1; c0 += 64) {
+    const int64_t t = c0 + lane;
+    const bool valid = t < s1;
+    int32_t l = valid ? lab[t] : 0;
+    if (l < 0 || l >= C) l = C;
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (l >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    int32_t base = 0;
+    if (valid) base = cur[wave][l];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int rank = __popcll(same & below);
+      out[base + rank] = (int32_t)t;
+      if (rank == 0) cur[wave][l] = base + __popcll(same);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One thread moves 16 bytes (8 bf16); a row of d elements is d/8 threads.
+template <bool kScatter>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint16_t *__restrict__ src,
+                                                           uint16_t *__restrict__ dst,
+                                                           const int32_t *__restrict__ perm,
+                                                           int H, int64_t N, int chunks,
+                                                           int64_t ss0, int64_t ss1, int64_t ss2,
+                                                           int64_t ds0, int64_t ds1, int64_t ds2,
+                                                           int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int64_t row = gid / chunks;
+  const int c = (int)(gid - row * chunks);
+  const int64_t bh = row / N, i = row - bh * N;
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t j = perm[row];
+  const bool ok = j >= 0 && j < N;
+  if (kScatter) {
+    if (!ok) return;
+    const uint4 x = *reinterpret_cast<const uint4 *>(src + b * ss0 + h * ss1 + i * ss2 + c * 8);
+    *reinterpret_cast<uint4 *>(dst + b * ds0 + h * ds1 + j * ds2 + c * 8) = x;
+  } else {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (ok) x = *reinterpret_cast<const uint4 *>(src + b * ss0 + h * ss1 + j * ss2 + c * 8);
+    *reinterpret_cast<uint4 *>(dst + b * ds0 + h * ds1 + i * ds2 + c * 8) = x;
+  }
+}
+
+template <bool kScatter>
+int permute_common(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H, int64_t N,
+                   int32_t d, const int64_t ss[3], const int64_t ds[3], bsa_stream_t stream) {
+  if (!src || !dst || !perm || !ss || !ds || B <= 0 || H <= 0 || N <= 0) return BSA_ERR_ARG;
+  if (d != 64 && d != 128) return BSA_ERR_UNSUPPORTED;
+  if (!bsa_aligned16(src) || !bsa_aligned16(dst)) return BSA_ERR_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (ss[i] < 0 || ds[i] < 0 || (ss[i] & 7) || (ds[i] & 7)) return BSA_ERR_ARG;
+  if (src == dst) return BSA_ERR_ARG;
+  const int chunks = d / 8;
+  const int64_t total = (int64_t)B * H * N * chunks;
+  const int64_t grid = (total + 255) / 256;
+  if (grid >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(permute_rows_kernel<kScatter>, dim3((unsigned)grid), dim3(256), 0,
+                     bsa_hip_stream(stream), static_cast<const uint16_t *>(src),
+                     static_cast<uint16_t *>(dst), perm, H, N, chunks, ss[0], ss[1], ss[2], ds[0],
+                     ds[1], ds[2], total);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" int bsa_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_t n_clusters,
+                                    int32_t *perm, bsa_stream_t stream) {
+  if (!labels || !perm || BH < 0 || N < 0) return BSA_ERR_ARG;
+  if (n_clusters <= 0) return BSA_ERR_ARG;
+  if (n_clusters > kMaxClusters) return BSA_ERR_UNSUPPORTED;
+  if (N >= (int64_t(1) << 31) || BH >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  if (BH == 0 || N == 0) return BSA_OK;
+  hipLaunchKernelGGL(perm_from_labels_kernel, dim3((unsigned)BH), dim3(256), 0,
+                     bsa_hip_stream(stream), labels, N, n_clusters, perm);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}
+
+extern "C" int bsa_permute_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
+                                int64_t N, int32_t d, const int64_t src_strides[3],
+                                const int64_t dst_strides[3], bsa_stream_t stream) {
+  return permute_common<false>(src, dst, perm, B, H, N, d, src_strides, dst_strides, stream);
+}
+
+extern "C" int bsa_unpermute_rows(const void *src, void *dst, const int32_t *perm, int32_t B,
+                                  int32_t H, int64_t N, int32_t d, const int64_t src_strides[3],
+                                  const int64_t dst_strides[3], bsa_stream_t stream) {
+  return permute_common<true>(src, dst, perm, B, H, N, d, src_strides, dst_strides, stream);
+}

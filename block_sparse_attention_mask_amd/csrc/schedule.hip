@@ -1,0 +1,111 @@
+// Row schedule: the launch order of the attention kernel's workgroups.
+//
+// WaveAlign (section IV-D) cuts the row sequence into consecutive buckets of
+// at most W rows (one wave of concurrently running rows) and sorts each bucket
+// by descending nonzero-block count, so that long rows start first and short
+// rows fill the tail next to the following wave; heads run one after another
+// (section VI-B, sequential-head scheduling).  Here the row sequence is
+// KV-group-major, so the query heads that share a KV head (GQA) run side by
+// side on the same K/V blocks, and the order is a launch table read by the
+// attention kernel: no data moves.
+//
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with a private L2.  With n_xcd > 1 the sorted sequence is dealt so that XCD
+// x receives the x-th contiguous slice, keeping neighbouring rows (which
+// share K/V blocks) in one L2.
+//
+// One workgroup per bucket: keys (INT32_MAX - nnz) << 32 | position are
+// sorted ascending with a bitonic network in LDS.
+#include "bsa_internal.h"
+
+namespace {
+
+constexpr int kMaxWave = 2048;
+
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ row_ptr, int Hq,
+                                                        int Hkv, int nQB, int W, int n_xcd,
+                                                        int64_t R, int32_t *__restrict__ order) {
+  __shared__ uint64_t key[kMaxWave];
+  const int G = Hq / Hkv;
+  const int64_t seg = (int64_t)G * nQB;
+  const int64_t nbk = (seg + W - 1) / W;           // buckets per (b, g) segment
+  const int64_t s = blockIdx.x / nbk, k = blockIdx.x % nbk;
+  const int64_t start = s * seg + k * W;           // logical position of the bucket's first row
+  const int n = (int)((k + 1) * W <= seg ? W : seg - k * W);
+  int P2 = 1;
+  while (P2 < n) P2 <<= 1;
+  const int64_t b = s / Hkv, g = s % Hkv;
+  for (int i = threadIdx.x; i < P2; i += 1024) {
+    uint64_t kk = ~0ull;
+    if (i < n) {
+      const int64_t j = k * W + i;                  // position within the segment
+      const int64_t u = j / G, hh = j % G;
+      const int64_t r = (b * Hq + g * G + hh) * nQB + u;
+      const int32_t nnz = row_ptr[r + 1] - row_ptr[r];
+      kk = ((uint64_t)(uint32_t)(0x7fffffff - nnz) << 32) | (uint32_t)i;
+    }
+    key[i] = kk;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P2 / 2; i += 1024) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = key[lo], c = key[hi];
+        if ((a > c) == up) {
+          key[lo] = c;
+          key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int src = (int)(key[i] & 0xffffffffu);
+    const int64_t j = k * W + src;
+    const int64_t u = j / G, hh = j % G;
+    const int32_t r = (int32_t)((b * Hq + g * G + hh) * nQB + u);
+    const int64_t P = start + i;                    // logical position
+    int64_t launch = P;
+    if (n_xcd > 1) {
+      int64_t st = 0;
+      for (int x = 0; x < n_xcd; ++x) {
+        const int64_t cnt = x < R ? (R - 1 - x) / n_xcd + 1 : 0;
+        if (P < st + cnt) {
+          launch = (P - st) * n_xcd + x;
+          break;
+        }
+        st += cnt;
+      }
+    }
+    order[launch] = r;
+  }
+}
+
+}  // namespace
+
+extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
+                            int32_t wave_rows, int32_t n_xcd, int32_t *order, bsa_stream_t stream) {
+  if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
+  if (Hq % Hkv) return BSA_ERR_ARG;
+  if (wave_rows < 0 || n_xcd < 0 || n_xcd > 64) return BSA_ERR_ARG;
+  if (wave_rows > kMaxWave) return BSA_ERR_UNSUPPORTED;
+  const int64_t R = (int64_t)B * Hq * nQB;
+  if (R >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  int W = wave_rows;
+  if (W == 0) {
+    int cus = bsa_device_cus();
+    if (cus < 0) return cus;
+    W = cus / (n_xcd > 1 ? n_xcd : 1);
+    if (W < 1) W = 1;
+    if (W > kMaxWave) W = kMaxWave;
+  }
+  const int64_t seg = (int64_t)(Hq / Hkv) * nQB;
+  const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
+  hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),
+                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, order);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}

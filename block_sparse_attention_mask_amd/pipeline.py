@@ -1,0 +1,104 @@
+"""One pass of the whole block-sparse attention path on device tensors:
+
+mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill)
+-> [cluster labels -> permutations; gather Q, K, V]   (permuted workloads)
+-> row schedule (bsa_schedule)
+-> attention forward (bsa_attn_fwd), with the inverse query permutation fused
+   into the output store, or applied by bsa_unpermute_rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import api
+
+
+@dataclass
+class DeviceWorkload:
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    block: int
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    mask: Optional[torch.Tensor] = None
+    T: Optional[torch.Tensor] = None
+    p: float = 0.0
+    lw_map: Optional[torch.Tensor] = None
+    labels_q: Optional[torch.Tensor] = None
+    labels_k: Optional[torch.Tensor] = None
+    n_clusters: int = 0
+    causal: bool = False
+    force_diag: bool = True
+
+    @property
+    def nQB(self) -> int:
+        return -(-self.N // self.block)
+
+    @property
+    def permuted(self) -> bool:
+        return self.labels_q is not None
+
+
+def to_device(w, device="cuda") -> DeviceWorkload:
+    """Copy a host workload (numpy arrays of bf16 bits etc.) to device tensors."""
+    t = lambda a, dt=None: None if a is None else torch.from_numpy(
+        np.ascontiguousarray(a if dt is None else a.view(dt))).to(device)
+    return DeviceWorkload(w.B, w.Hq, w.Hkv, w.N, w.d, w.block,
+                          t(w.q, np.int16), t(w.k, np.int16), t(w.v, np.int16),
+                          t(w.mask), t(w.T), float(w.p), t(w.lw_map), t(w.labels_q), t(w.labels_k),
+                          int(w.n_clusters), bool(w.causal), bool(w.force_diag))
+
+
+@dataclass
+class StepResult:
+    out: torch.Tensor
+    lse: Optional[torch.Tensor]
+    row_ptr: torch.Tensor
+    col: torch.Tensor
+    lw: Optional[torch.Tensor]
+    order: Optional[torch.Tensor]
+    perm_q: Optional[torch.Tensor] = None
+    perm_k: Optional[torch.Tensor] = None
+
+
+def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
+            fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
+            stream=None) -> StepResult:
+    """Run every step of the path once.  ``attn_events`` (start, end) are
+    recorded around the attention launch on the same stream."""
+    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag,
+                                     stream=stream)
+    q, k, v = dw.q, dw.k, dw.v
+    perm_q = perm_k = None
+    if dw.permuted:
+        perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=stream)
+        perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=stream)
+        q = api.permute_rows(dw.q, perm_q, stream=stream)
+        k = api.permute_rows(dw.k, perm_k, stream=stream)
+        v = api.permute_rows(dw.v, perm_k, stream=stream)
+    order = None
+    if schedule:
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream)
+    sperm = perm_q if (dw.permuted and fuse_scatter) else None
+    s = stream if stream is not None else torch.cuda.current_stream()
+    if attn_events is not None:
+        attn_events[0].record(s)
+    out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
+                            want_lse=want_lse, causal=dw.causal, stream=stream)
+    if attn_events is not None:
+        attn_events[1].record(s)
+    if dw.permuted and not fuse_scatter:
+        out = api.unpermute_rows(out, perm_q, stream=stream)
+        if lse is not None:
+            inv = torch.empty_like(lse)
+            inv.scatter_(1, perm_q.long(), lse)
+            lse = inv
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)

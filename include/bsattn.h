@@ -1,0 +1,194 @@
+/*
+ * bsattn.h -- block-sparse (optionally permuted) softmax attention forward on
+ * AMD Instinct MI355X (gfx950).  C ABI of libbsattn.so.
+ *
+ * Terminology
+ *   B, Hq, Hkv, N, d   batch, query heads, key/value heads (Hq % Hkv == 0),
+ *                      tokens, head dimension.
+ *   block              query block size = key block size (64 or 128).
+ *   nQB = nKB          ceil(N / block); the last block may be partial.
+ *   row                one (batch, query head, query block) triple,
+ *                      r = (b * Hq + h) * nQB + u, R = B * Hq * nQB rows.
+ *   CSR                row_ptr[R + 1] (int32) and col[nnz] (int32, ascending
+ *                      KV-block indices per row), optional lw[nnz] (float32
+ *                      additive log-weight of each listed block).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument that names device memory must be device memory
+ *     allocated by the caller; the library never allocates or frees device
+ *     memory and keeps no state between calls.
+ *   - Work is enqueued on the caller's HIP stream and is asynchronous, except
+ *     bsa_csr_count, which synchronises the stream to return nnz.
+ *   - Return value: BSA_OK (0) or a negative BSA_ERR_* code.  Argument checks
+ *     run on the host before any HIP call; on an argument error nothing is
+ *     enqueued.  BSA_ERR_HIP reports a failed launch or HIP runtime call.
+ *   - Token-major tensors are addressed with int64 element strides for
+ *     (batch, head, token); the head dimension must be contiguous, base
+ *     pointers 16-byte aligned and strides multiples of 8 elements.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_OK 0
+#define BSA_ERR_ARG (-1)         /* null pointer, bad size, stride or alignment */
+#define BSA_ERR_UNSUPPORTED (-2) /* d or block not in {64,128}, causal with a permutation, size limits */
+#define BSA_ERR_CAPACITY (-3)    /* an output array is too small */
+#define BSA_ERR_HIP (-4)         /* HIP runtime or launch failure */
+
+typedef void *bsa_stream_t; /* a hipStream_t; NULL is the default stream */
+
+/* Library version, (major << 16) | minor. */
+int bsa_version(void);
+
+/* Static description of an error code (never NULL). */
+const char *bsa_strerror(int code);
+
+/* ---------------------------------------------------------------------------
+ * Mask -> CSR, pass 1.
+ *
+ * Source: ScalingAttention (section 5.2, Eq. 2) instantiates the block mask of
+ * density p from a threshold map as M_p = I(T <= p); the block-sparse mask of
+ * WaveAlign (section II-B) has one row per query block whose retained entries
+ * are the executed (query block, KV block) interactions.
+ *
+ * Entry (r, v) is kept when mask[r * nKB + v] != 0 (if mask != NULL), else
+ * when T[r * nKB + v] <= p (float32 comparison; NaN is never kept), or when
+ * force_diag != 0 and v == r % nQB (the diagonal block, so that no row is
+ * empty).  Exactly one of mask (uint8, device) and T (float32, device) must be
+ * non-NULL; both are [R][nKB] row-major.
+ *
+ * Writes row_ptr[0..R] (device, int32, caller-owned, R + 1 entries) and stores
+ * nnz = row_ptr[R] into *nnz_out (host).  Synchronises `stream`.
+ * Errors: BSA_ERR_ARG for NULL/negative sizes or both/neither sources;
+ * BSA_ERR_UNSUPPORTED when R * nKB >= 2^31 or force_diag with nQB > nKB.
+ * ------------------------------------------------------------------------- */
+int bsa_csr_count(const uint8_t *mask, const float *T, float p, int64_t R, int32_t nQB,
+                  int32_t nKB, int force_diag, int32_t *row_ptr, int64_t *nnz_out,
+                  bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Mask -> CSR, pass 2.  Same keep rule and arguments as bsa_csr_count, with
+ * row_ptr as it produced.  Writes col[row_ptr[r] ..] = kept v of row r in
+ * ascending order (the order of the CRM forward iterator of ScalingAttention,
+ * section 7.3, Algorithm 2).  When lw != NULL also writes lw[e] = the bits of
+ * lw_map[r * nKB + v] (float32 [R][nKB], device), or 0.0f when lw_map is
+ * NULL.  `capacity` is the number of entries col (and lw) can hold; it must
+ * be >= nnz (BSA_ERR_CAPACITY otherwise, checked on the device copy of
+ * row_ptr[R] only through the caller: entries at index >= capacity are never
+ * written).  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_csr_fill(const uint8_t *mask, const float *T, float p, const float *lw_map, int64_t R,
+                 int32_t nQB, int32_t nKB, int force_diag, const int32_t *row_ptr, int32_t *col,
+                 float *lw, int64_t capacity, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Cluster labels -> gather permutation.
+ *
+ * Source: permuted block-sparse attention clusters queries and keys and
+ * permutes the tokens so that every cluster is contiguous (InstaGen,
+ * section 4; WaveAlign, section IV-A: rows are permuted and outputs
+ * restored).
+ *
+ * labels: int32 [BH][N] (device).  perm: int32 [BH][N] (device, output):
+ * perm[bh][i] is the original index of the token placed at position i; the
+ * order is ascending (label, original index), so equal labels keep their
+ * original order.  Labels outside [0, n_clusters) sort after all valid
+ * labels.  n_clusters must be in [1, 16384].  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_t n_clusters,
+                         int32_t *perm, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Row gather / scatter of a [B][H][N][d] bf16 tensor by a per-(b,h)
+ * permutation perm [B*H][N] (device, int32, gather form as above).
+ *   bsa_permute_rows:   dst[b][h][i]       = src[b][h][perm[bh][i]]
+ *   bsa_unpermute_rows: dst[b][h][perm[bh][i]] = src[b][h][i]
+ * (WaveAlign, section V: permute query rows before attention and restore the
+ * output order after it.)  src and dst are bf16 (uint16 bits), strides in
+ * elements for (batch, head, token); d in {64, 128}; src and dst must not
+ * overlap.  An index outside [0, N) is skipped (gather writes zeros).
+ * Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_permute_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
+                     int64_t N, int32_t d, const int64_t src_strides[3],
+                     const int64_t dst_strides[3], bsa_stream_t stream);
+int bsa_unpermute_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
+                       int64_t N, int32_t d, const int64_t src_strides[3],
+                       const int64_t dst_strides[3], bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Row schedule (launch order of the attention kernel).
+ *
+ * Source: WaveAlign, section IV-D (rows in consecutive buckets of at most W,
+ * each bucket sorted by descending nonzero-block count, long rows first) and
+ * section VI-B (sequential-head scheduling).
+ *
+ * Logical sequence: for each batch b and KV head g, the rows of the
+ * G = Hq / Hkv query heads sharing g, query block u outer and head inner
+ * (identity stage-1 order).  Buckets of `wave_rows` consecutive entries within
+ * each (b, g) segment are sorted by (nnz descending, sequence position
+ * ascending).  When n_xcd > 1 the list is dealt to launch indices so that the
+ * GPU's round-robin dispatch gives XCD x the x-th contiguous slice:
+ * order[i] = logical[start(i % n_xcd) + i / n_xcd].  wave_rows = 0 selects
+ * (compute units / max(1, n_xcd)).  row_ptr: device int32 [R+1];
+ * order: device int32 [R] (output).  wave_rows <= 2048.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
+                 int32_t wave_rows, int32_t n_xcd, int32_t *order, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention forward.
+ *
+ * Source: InstaGen, section 3.1 Eq. (1)-(3) (l_ij = q_i . k_j / sqrt(d),
+ * o_i = sum_j softmax_j(l_ij) v_j) restricted to the KV blocks listed for the
+ * query's block row (WaveAlign, section II-B), with the listed block's
+ * log-weight added to the scaled logit (InstaGen, Algorithm 1: softmax of
+ * l_ij + log w_j with Horvitz-Thompson weights).  Masked pairs contribute
+ * nothing.  With causal != 0, key s is also masked for query t when s > t
+ * (token positions; not allowed together with a permutation).  Keys and
+ * queries at positions >= N in the last block do not take part.
+ *
+ * q [B][Hq][N][d], k and v [B][Hkv][N][d], o [B][Hq][N][d]: bf16 (uint16 bits)
+ * device tensors addressed by the strides; query head h reads KV head
+ * h / (Hq / Hkv).  o must not alias q, k or v.  lse (float32 [B*Hq][N],
+ * contiguous, device, optional) receives ln(sum_j exp(l_ij + log w_j)) of
+ * every query.  row_ptr/col/lw: CSR as built above (lw optional).  order
+ * (optional, int32 [R]): launch index -> row; rows not listed are not
+ * computed.  scatter_perm_q (optional, int32 [B*Hq][N]): when set, the output
+ * of the query at position i is written to position scatter_perm_q[bh][i] of
+ * o (and lse), i.e. the inverse permutation is fused into the store.
+ * scale <= 0 selects 1/sqrt(d).  A row with an empty list writes O = 0 and
+ * LSE = -inf.  Log-weights must be finite or -inf.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int32_t B, Hq, Hkv, d, block;
+  int64_t N;
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3];
+  const int32_t *row_ptr, *col;
+  const float *lw;
+  const int32_t *order;
+  int64_t n_order; /* entries of order (launch count); 0 = R */
+  const int32_t *scatter_perm_q;
+  float scale;
+  int32_t causal;
+} bsa_attn_args;
+
+int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);
+
+/* Number of compute units of the current device (for wave sizing), or a
+ * negative error. */
+int bsa_device_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSATTN_H */

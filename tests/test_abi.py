@@ -1,0 +1,114 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/bsattn.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented error codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_mask_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "bsattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_attention_mask_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(_lib.EXPORTS)
+
+
+def test_version_and_strerror(L):
+    assert L.bsa_version() >= 1
+    for code in (0, -1, -2, -3, -4, -99):
+        assert L.bsa_strerror(code)
+
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: the calls fail argument checks first
+
+
+def test_csr_argument_errors(L):
+    n = _lib.I64(0)
+    # neither and both sources
+    assert L.bsa_csr_count(None, None, 0.5, 4, 2, 2, 1, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_count(FAKE, FAKE, 0.5, 4, 2, 2, 1, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_count(FAKE, None, 0.5, -1, 2, 2, 1, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_count(FAKE, None, 0.5, 4, 2, 2, 1, None, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_count(FAKE, None, 0.5, 4, 2, 2, 1, FAKE, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_count(FAKE, None, 0.5, 1 << 30, 4, 4, 1, FAKE, ctypes.byref(n), None) == \
+        _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_csr_count(FAKE, None, 0.5, 4, 3, 2, 1, FAKE, ctypes.byref(n), None) == \
+        _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_csr_fill(FAKE, None, 0.5, None, 4, 2, 2, 1, FAKE, FAKE, None, -1, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_csr_fill(FAKE, None, 0.5, None, 4, 2, 2, 1, FAKE, None, None, 5, None) == _lib.BSA_ERR_ARG
+
+
+def test_perm_argument_errors(L):
+    assert L.bsa_perm_from_labels(None, 2, 10, 4, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_perm_from_labels(FAKE, 2, 10, 0, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_perm_from_labels(FAKE, 2, 10, 5000, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    st = _lib.I64x3(1024, 128, 8)
+    bad = _lib.I64x3(1024, 128, 3)
+    assert L.bsa_permute_rows(FAKE, ctypes.c_void_p(8192), FAKE, 1, 1, 8, 96, st, st, None) == \
+        _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_permute_rows(FAKE, ctypes.c_void_p(8192), FAKE, 1, 1, 8, 128, bad, st, None) == \
+        _lib.BSA_ERR_ARG
+    assert L.bsa_permute_rows(ctypes.c_void_p(4100), ctypes.c_void_p(8192), FAKE, 1, 1, 8, 128, st, st,
+                              None) == _lib.BSA_ERR_ARG
+    assert L.bsa_unpermute_rows(FAKE, FAKE, FAKE, 1, 1, 8, 128, st, st, None) == _lib.BSA_ERR_ARG
+
+
+def test_schedule_argument_errors(L):
+    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, FAKE, None) == _lib.BSA_ERR_ARG
+
+
+def _args(**kw):
+    a = _lib.AttnArgs()
+    a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
+    a.B, a.Hq, a.Hkv, a.d, a.block, a.N = 1, 4, 2, 128, 128, 1000
+    st = _lib.I64x3(4 * 1000 * 128, 1000 * 128, 128)
+    a.q_str = a.k_str = a.v_str = a.o_str = st
+    a.row_ptr, a.col = FAKE, FAKE
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.BSA_ERR_ARG),
+    (dict(row_ptr=None), _lib.BSA_ERR_ARG),
+    (dict(d=96), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(block=32), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(Hq=3), _lib.BSA_ERR_ARG),
+    (dict(N=0), _lib.BSA_ERR_ARG),
+    (dict(causal=1, scatter_perm_q=FAKE), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(q=ctypes.c_void_p(4104)), _lib.BSA_ERR_ARG),
+    (dict(q_str=_lib.I64x3(4 * 1000 * 128, 1000 * 128, 130)), _lib.BSA_ERR_ARG),
+    (dict(o=FAKE), _lib.BSA_ERR_ARG),
+    (dict(order=FAKE, n_order=10 ** 6), _lib.BSA_ERR_ARG),
+    (dict(N=1 << 40), _lib.BSA_ERR_UNSUPPORTED),
+])
+def test_attn_argument_errors(L, kw, code):
+    a = _args(**kw)
+    assert L.bsa_attn_fwd(ctypes.byref(a), None) == code
+    assert L.bsa_attn_fwd(None, None) == _lib.BSA_ERR_ARG
