@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = one pass of the whole block-sparse attention path
+(threshold map -> CSR, cluster labels -> permutations, Q/K/V gather, row
+schedule, attention forward with fused scatter-back) on a synthetic
+Wan2.1-14B-shaped 720p video DiT self-attention (1 x 40 heads x 75600 tokens,
+d = 128, 128x128 blocks, 64 Gaussian clusters per head, KV blocks kept to
+cumulative mass 0.9, ~15 % density).
+
+Prints one JSON line.  ``value`` is effective TFLOPS of the whole step
+(4*d FLOPs per allowed query-key pair / step time); ``roofline`` is measured
+on the attention kernel alone with HIP events on its stream; ``cpu_baseline``
+times the CPU reference checker on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd effective TFLOPS & % bf16 MFMA peak, Wan2.1-14B shape"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="clustered",
+                    choices=["clustered", "importance_sampled", "video_threshold", "llm_prefill", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for HBM counter scaling)")
+    ap.add_argument("--n-xcd", type=int, default=8)
+    ap.add_argument("--wave-rows", type=int, default=0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_sparse_attention_mask_amd import _lib, metrics, pipeline, synth
+    if not os.path.exists(_lib.LIB_PATH):
+        raise SystemExit("libbsattn.so is not built; run python __graft_entry__.py first")
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    w = synth.CONFIGS[args.config]()
+    log("generated %s in %.1fs" % (args.config, time.time() - t0))
+    dw = pipeline.to_device(w, dev)
+    stream = torch.cuda.current_stream()
+
+    # one pass to get the CSR for the work count (outside the timed region)
+    res = pipeline.forward(dw, n_xcd=args.n_xcd, wave_rows=args.wave_rows)
+    torch.cuda.synchronize()
+    rp = res.row_ptr.cpu().numpy()
+    col = res.col.cpu().numpy()
+    pairs = metrics.count_pairs(rp, col, w.N, w.block, w.causal)
+    eff_flops = 4.0 * w.d * pairs
+    nnz = int(rp[-1])
+    density = nnz / float(w.R * w.nKB)
+    log("nnz %d density %.4f pairs %d eff GFLOP %.1f" % (nnz, density, pairs, eff_flops / 1e9))
+
+    for _ in range(args.warmup):
+        pipeline.forward(dw, n_xcd=args.n_xcd, wave_rows=args.wave_rows)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        pipeline.forward(dw, n_xcd=args.n_xcd, wave_rows=args.wave_rows, attn_events=evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_step = t_total * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg = float(np.mean(attn_ms))
+    attn_med = float(np.median(attn_ms))
+    value = eff_flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = eff_flops / (attn_avg * 1e-3) / 1e12
+    log("step %.3f ms, attention avg %.3f ms (median %.3f) -> %.1f TFLOPS kernel, %.1f TFLOPS step"
+        % (ms_step, attn_avg, attn_med, attn_tflops, value))
+
+    # stage breakdown (one extra, separately synchronised pass; not part of value)
+    stages = stage_times(pipeline, dw, args, torch)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        src = torch.empty(n, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB x3 (torch copy kernel)" % args.copy_probe_mib)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, rp, col, res, args.cpu_seconds, metrics)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload_name(args.config),
+            "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "seq_len": w.N, "head_dim": w.d,
+            "block": w.block, "nnz_blocks": nnz, "block_density": round(density, 5),
+            "allowed_pairs": pairs, "effective_gflop": round(eff_flops / 1e9, 3),
+            "permuted": bool(w.permuted), "causal": bool(w.causal), "log_weights": w.lw_map is not None,
+            "schedule": {"n_xcd": args.n_xcd, "wave_rows": args.wave_rows or "auto"},
+            "parallelism": "single-gpu",
+        },
+        "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "attn_kernel": {"avg_ms": round(attn_avg, 4), "median_ms": round(attn_med, 4),
+                        "tflops": round(attn_tflops, 2),
+                        "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2)},
+        "stages_ms": stages,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "attn_fwd_kernel<128,128>",
+                     "per_unit": "4*d = 512 FLOP per allowed query-key pair",
+                     "units_per_launch": pairs},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def workload_name(cfg):
+    return {
+        "clustered": "Wan2.1-14B 720p video DiT self-attention, clustered+permuted block-sparse "
+                     "(1x40x75600, d128, 128x128 blocks, cumulative mass 0.9)",
+        "importance_sampled": "Wan2.1-14B shape, group-shared importance-sampled blocks with log-weights",
+        "video_threshold": "Wan2.1-1.3B video DiT shape, threshold map T<=p (1x12x32760)",
+        "llm_prefill": "LLaMA-3.1-8B prefill shape, causal GQA static block pattern (32q/8kv x 65536)",
+        "tiny": "tiny 1x2x1024 d64, 64x64 blocks, 25% random mask",
+    }[cfg]
+
+
+def stage_times(pipeline, dw, args, torch):
+    from block_sparse_attention_mask_amd import api
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    torch.cuda.synchronize()
+    ev[0].record(s)
+    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
+    ev[1].record(s)
+    q, k, v, pq = dw.q, dw.k, dw.v, None
+    if dw.permuted:
+        pq = api.perm_from_labels(dw.labels_q, dw.n_clusters)
+        pk = api.perm_from_labels(dw.labels_k, dw.n_clusters)
+        q = api.permute_rows(dw.q, pq)
+        k = api.permute_rows(dw.k, pk)
+        v = api.permute_rows(dw.v, pk)
+    ev[2].record(s)
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd)
+    ev[3].record(s)
+    api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
+                 causal=dw.causal)
+    ev[4].record(s)
+    torch.cuda.synchronize()
+    names = ["mask_to_csr", "perm_and_gather", "schedule", "attention_fused_scatter"]
+    return {n: round(ev[i].elapsed_time(ev[i + 1]), 4) for i, n in enumerate(names)}
+
+
+def cpu_baseline(w, rp, col, res, target_s, metrics):
+    """The CPU reference checker on a bounded, seeded sample of query rows of
+    the same workload; rate in effective TFLOPS (same 4*d per pair)."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    pq = res.perm_q.cpu().numpy() if res.perm_q is not None else None
+    pk = res.perm_k.cpu().numpy() if res.perm_k is not None else None
+    lw = res.lw.cpu().numpy() if res.lw is not None else None
+    rng = np.random.default_rng(1234)
+    per_row = metrics.pairs_per_row(rp, col, w.N, w.block, w.causal)   # per block row
+    total_rows = w.B * w.Hq * w.N
+
+    def run(n):
+        rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+        bh, t = rows // w.N, rows % w.N
+        pos = pq[bh, t] if pq is not None else t
+        r = bh * w.nQB + pos // w.block
+        nq = np.minimum(w.block, w.N - (pos // w.block) * w.block)
+        # pairs of one query row = pairs of its block row / real queries of the block
+        # (exact when not causal; causal uses the diagonal's own row count)
+        if w.causal:
+            pr = np.array([row_pairs_causal(rp, col, int(rr), int(tt), w) for rr, tt in zip(r, pos)])
+        else:
+            pr = per_row[r] // nq
+        t0 = time.perf_counter()
+        oracle.attn_rows(w.q, w.k, w.v, rp, col, lw, w.block, rows, pq, pk, w.causal)
+        return time.perf_counter() - t0, float(pr.sum()), n
+
+    dt, pr, n = run(256)
+    rate = pr / max(dt, 1e-9)
+    n2 = int(min(total_rows, max(256, target_s * 256 / max(dt, 1e-9))))
+    if dt < target_s / 2:
+        dt, pr, n = run(n2)
+    value = 4.0 * w.d * pr / dt / 1e12
+    return {"value": value, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": "%d seeded random query rows of the same workload (all heads), fp64 "
+                      "dense-masked oracle, %.1f s" % (n, dt),
+            "seconds": round(dt, 3), "rows": n}
+
+
+def row_pairs_causal(rp, col, r, t, w):
+    u = t // w.block
+    tot = 0
+    for e in range(rp[r], rp[r + 1]):
+        v = int(col[e])
+        nk = min(w.block, w.N - v * w.block)
+        if v < u:
+            tot += nk
+        elif v == u:
+            tot += t - u * w.block + 1
+    return tot
+
+
+if __name__ == "__main__":
+    main()
