@@ -15,12 +15,13 @@ I64x3 = ctypes.c_int64 * 3
 BSA_OK = 0
 BSA_ERR_ARG = -1
 BSA_ERR_UNSUPPORTED = -2
-BSA_ERR_CAPACITY = -3
 BSA_ERR_HIP = -4
+BSA_V_TOKEN_MAJOR = 0
+BSA_V_DIM_MAJOR = 1
 
 # Every symbol include/bsattn.h declares.
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_perm_from_labels",
-           "bsa_permute_rows", "bsa_unpermute_rows", "bsa_schedule", "bsa_attn_fwd",
+           "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_schedule", "bsa_attn_fwd",
            "bsa_device_cus")
 
 
@@ -35,6 +36,7 @@ class AttnArgs(ctypes.Structure):
         ("scatter_perm_q", P),
         ("scale", ctypes.c_float),
         ("causal", I32),
+        ("v_layout", I32),
     ]
 
 
@@ -71,6 +73,8 @@ def load():
         for fn in (L.bsa_permute_rows, L.bsa_unpermute_rows):
             fn.restype = ctypes.c_int
             fn.argtypes = [P, P, P, I32, I32, I64, I32, P, P, P]
+        L.bsa_transpose_rows.restype = ctypes.c_int
+        L.bsa_transpose_rows.argtypes = [P, P, P, I32, I32, I64, I32, I64, P, P, P]
         L.bsa_schedule.restype = ctypes.c_int
         L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P]
         L.bsa_attn_fwd.restype = ctypes.c_int

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import AttnArgs, I64, I64x3, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
-           "unpermute_rows", "schedule", "attn_fwd", "device_cus"]
+           "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus"]
 
 _BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
 
@@ -136,6 +136,24 @@ def unpermute_rows(src, perm, dst=None, stream=None):
     return _permute("bsa_unpermute_rows", src, perm, dst, stream)
 
 
+def transpose_rows(src: torch.Tensor, perm: Optional[torch.Tensor] = None, ld: Optional[int] = None,
+                   dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dst[b][h][c][i] = src[b][h][perm[b*H + h][i] (or i)][c] for i < N, zeros
+    for N <= i < ld: the dim-major V the attention kernel reads."""
+    _dev(src, "src", _BF16_LIKE)
+    B, H, N, d = src.shape
+    if ld is None:
+        ld = -(-N // 128) * 128
+    if dst is None:
+        dst = torch.empty((B, H, d, ld), dtype=src.dtype, device=src.device)
+    if perm is not None:
+        _dev(perm, "perm", torch.int32)
+        perm = perm.contiguous()
+    check("bsa_transpose_rows", load().bsa_transpose_rows(_ptr(src), _ptr(dst), _ptr(perm), B, H, N, d, int(ld),
+                                                          _strides(src), _strides(dst), _stream(stream)))
+    return dst
+
+
 def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_rows: int = 0,
              n_xcd: int = 8, order=None, stream=None) -> torch.Tensor:
     _dev(row_ptr, "row_ptr", torch.int32)
@@ -150,8 +168,11 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.T
              col: torch.Tensor, block: int, lw: Optional[torch.Tensor] = None,
              order: Optional[torch.Tensor] = None, scatter_perm_q: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             want_lse: bool = False, scale: float = 0.0, causal: bool = False, stream=None):
-    """Block-sparse attention forward; returns (out, lse or None)."""
+             want_lse: bool = False, scale: float = 0.0, causal: bool = False,
+             v_dim_major: bool = False, stream=None):
+    """Block-sparse attention forward; returns (out, lse or None).  With
+    ``v_dim_major`` v is [B][Hkv][d][ld] (keys contiguous, from transpose_rows),
+    otherwise [B][Hkv][N][d]."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     B, Hq, N, d = q.shape
@@ -171,5 +192,6 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.T
     a.scatter_perm_q = _ptr(scatter_perm_q)
     a.scale = float(scale)
     a.causal = int(bool(causal))
+    a.v_layout = _lib.BSA_V_DIM_MAJOR if v_dim_major else _lib.BSA_V_TOKEN_MAJOR
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse

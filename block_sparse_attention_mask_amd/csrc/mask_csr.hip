@@ -152,7 +152,6 @@ extern "C" const char *bsa_strerror(int code) {
     case BSA_OK: return "ok";
     case BSA_ERR_ARG: return "invalid argument";
     case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case BSA_ERR_CAPACITY: return "output capacity too small";
     case BSA_ERR_HIP: return "HIP runtime or launch failure";
     default: return "unknown error";
   }

@@ -140,7 +140,68 @@ int permute_common(const void *src, void *dst, const int32_t *perm, int32_t B, i
   return BSA_OK;
 }
 
+// Gather + transpose: one thread turns an 8-token x 8-dim block into an
+// 8-dim x 8-token block in registers (16-byte loads along d, 16-byte stores
+// along tokens).  Threads are d-chunk fastest so that the gathered rows are
+// read with full 256-byte segments.
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t *__restrict__ src,
+                                                             uint16_t *__restrict__ dst,
+                                                             const int32_t *__restrict__ perm,
+                                                             int H, int64_t N, int chunks, int64_t ld8,
+                                                             int64_t ss0, int64_t ss1, int64_t ss2,
+                                                             int64_t ds0, int64_t ds1, int64_t ds2,
+                                                             int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int c = (int)(gid % chunks);                 // 8-dim chunk
+  const int64_t rest = gid / chunks;
+  const int64_t tg = rest % ld8;                     // 8-token group
+  const int64_t bh = rest / ld8;
+  const int64_t b = bh / H, h = bh - b * H;
+  uint32_t w[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t i = tg * 8 + t;
+    int64_t j = -1;
+    if (i < N) j = perm ? (int64_t)perm[bh * N + i] : i;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (j >= 0 && j < N) x = *reinterpret_cast<const uint4 *>(src + b * ss0 + h * ss1 + j * ss2 + c * 8);
+    w[t][0] = x.x; w[t][1] = x.y; w[t][2] = x.z; w[t][3] = x.w;
+  }
+  uint16_t *out = dst + b * ds0 + h * ds1 + (int64_t)c * 8 * ds2 + tg * 8;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {   // dims 2q (low halves) and 2q+1 (high halves)
+    const uint4 lo = make_uint4((w[0][q] & 0xffffu) | (w[1][q] << 16), (w[2][q] & 0xffffu) | (w[3][q] << 16),
+                                (w[4][q] & 0xffffu) | (w[5][q] << 16), (w[6][q] & 0xffffu) | (w[7][q] << 16));
+    const uint4 hi = make_uint4((w[0][q] >> 16) | (w[1][q] & 0xffff0000u), (w[2][q] >> 16) | (w[3][q] & 0xffff0000u),
+                                (w[4][q] >> 16) | (w[5][q] & 0xffff0000u), (w[6][q] >> 16) | (w[7][q] & 0xffff0000u));
+    *reinterpret_cast<uint4 *>(out + (2 * q) * ds2) = lo;
+    *reinterpret_cast<uint4 *>(out + (2 * q + 1) * ds2) = hi;
+  }
+}
+
 }  // namespace
+
+extern "C" int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
+                                  int64_t N, int32_t d, int64_t ld, const int64_t ss[3],
+                                  const int64_t ds[3], bsa_stream_t stream) {
+  if (!src || !dst || !ss || !ds || B <= 0 || H <= 0 || N <= 0) return BSA_ERR_ARG;
+  if (d != 64 && d != 128) return BSA_ERR_UNSUPPORTED;
+  if (ld < N || (ld & 7) || ds[2] < ld) return BSA_ERR_ARG;
+  if (!bsa_aligned16(src) || !bsa_aligned16(dst) || src == dst) return BSA_ERR_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (ss[i] < 0 || ds[i] < 0 || (ss[i] & 7) || (ds[i] & 7)) return BSA_ERR_ARG;
+  const int chunks = d / 8;
+  const int64_t ld8 = ld / 8;
+  const int64_t total = (int64_t)B * H * ld8 * chunks;
+  const int64_t grid = (total + 255) / 256;
+  if (grid >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)grid), dim3(256), 0, bsa_hip_stream(stream),
+                     static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), perm, H, N, chunks,
+                     ld8, ss[0], ss[1], ss[2], ds[0], ds[1], ds[2], total);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}
 
 extern "C" int bsa_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_t n_clusters,
                                     int32_t *perm, bsa_stream_t stream) {

@@ -1,7 +1,8 @@
 """One pass of the whole block-sparse attention path on device tensors:
 
 mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill)
--> [cluster labels -> permutations; gather Q, K, V]   (permuted workloads)
+-> [cluster labels -> permutations; gather Q, K]        (permuted workloads)
+-> V gathered (when permuted) and written dim-major (bsa_transpose_rows)
 -> row schedule (bsa_schedule)
 -> attention forward (bsa_attn_fwd), with the inverse query permutation fused
    into the output store, or applied by bsa_unpermute_rows.
@@ -71,7 +72,7 @@ class StepResult:
 
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
-            stream=None) -> StepResult:
+            v_dim_major: bool = True, stream=None) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream."""
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag,
@@ -83,7 +84,10 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
         perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=stream)
         q = api.permute_rows(dw.q, perm_q, stream=stream)
         k = api.permute_rows(dw.k, perm_k, stream=stream)
-        v = api.permute_rows(dw.v, perm_k, stream=stream)
+        if not v_dim_major:
+            v = api.permute_rows(dw.v, perm_k, stream=stream)
+    if v_dim_major:
+        v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=stream)
     order = None
     if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream)
@@ -92,7 +96,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     if attn_events is not None:
         attn_events[0].record(s)
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
-                            want_lse=want_lse, causal=dw.causal, stream=stream)
+                            want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if dw.permuted and not fuse_scatter:

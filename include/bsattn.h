@@ -38,10 +38,13 @@ extern "C" {
 #define BSA_OK 0
 #define BSA_ERR_ARG (-1)         /* null pointer, bad size, stride or alignment */
 #define BSA_ERR_UNSUPPORTED (-2) /* d or block not in {64,128}, causal with a permutation, size limits */
-#define BSA_ERR_CAPACITY (-3)    /* an output array is too small */
 #define BSA_ERR_HIP (-4)         /* HIP runtime or launch failure */
 
 typedef void *bsa_stream_t; /* a hipStream_t; NULL is the default stream */
+
+/* Layout of V for bsa_attn_fwd. */
+#define BSA_V_TOKEN_MAJOR 0 /* [B][Hkv][N][d]: strides (batch, head, token), d contiguous */
+#define BSA_V_DIM_MAJOR 1   /* [B][Hkv][d][ld]: strides (batch, head, dim row), keys contiguous */
 
 /* Library version, (major << 16) | minor. */
 int bsa_version(void);
@@ -78,10 +81,10 @@ int bsa_csr_count(const uint8_t *mask, const float *T, float p, int64_t R, int32
  * ascending order (the order of the CRM forward iterator of ScalingAttention,
  * section 7.3, Algorithm 2).  When lw != NULL also writes lw[e] = the bits of
  * lw_map[r * nKB + v] (float32 [R][nKB], device), or 0.0f when lw_map is
- * NULL.  `capacity` is the number of entries col (and lw) can hold; it must
- * be >= nnz (BSA_ERR_CAPACITY otherwise, checked on the device copy of
- * row_ptr[R] only through the caller: entries at index >= capacity are never
- * written).  Asynchronous.
+ * NULL.  `capacity` is the number of entries col (and lw) can hold and
+ * should be the nnz bsa_csr_count returned; entries at an index >= capacity
+ * are never written (the list is truncated, nothing faults).  BSA_ERR_ARG for
+ * capacity < 0 or col == NULL with capacity > 0.  Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_csr_fill(const uint8_t *mask, const float *T, float p, const float *lw_map, int64_t R,
                  int32_t nQB, int32_t nKB, int force_diag, const int32_t *row_ptr, int32_t *col,
@@ -99,7 +102,7 @@ int bsa_csr_fill(const uint8_t *mask, const float *T, float p, const float *lw_m
  * perm[bh][i] is the original index of the token placed at position i; the
  * order is ascending (label, original index), so equal labels keep their
  * original order.  Labels outside [0, n_clusters) sort after all valid
- * labels.  n_clusters must be in [1, 16384].  Asynchronous.
+ * labels.  n_clusters must be in [1, 4095].  Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_t n_clusters,
                          int32_t *perm, bsa_stream_t stream);
@@ -120,6 +123,22 @@ int bsa_permute_rows(const void *src, void *dst, const int32_t *perm, int32_t B,
                      const int64_t dst_strides[3], bsa_stream_t stream);
 int bsa_unpermute_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
                        int64_t N, int32_t d, const int64_t src_strides[3],
+                       const int64_t dst_strides[3], bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Gather + transpose into the dim-major layout bsa_attn_fwd reads fastest.
+ *   dst[b][h][c][i] = src[b][h][perm ? perm[bh][i] : i][c]   for i < N
+ *   dst[b][h][c][i] = 0                                       for N <= i < ld
+ * (the V side of the permutation step of permuted block-sparse attention,
+ * written key-contiguous so that the attention kernel's P.V contraction reads
+ * 16-byte rows).  src: bf16 [B][H][N][d], strides (batch, head, token), d
+ * contiguous.  dst: bf16, strides (batch, head, dim row), keys contiguous;
+ * dst_strides[2] >= ld; ld >= N and a multiple of 8; d in {64, 128}.
+ * perm (int32 [B*H][N], device) may be NULL.  An index outside [0, N) in perm
+ * gathers zeros.  src and dst must not overlap.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t B, int32_t H,
+                       int64_t N, int32_t d, int64_t ld, const int64_t src_strides[3],
                        const int64_t dst_strides[3], bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -154,9 +173,13 @@ int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int
  * (token positions; not allowed together with a permutation).  Keys and
  * queries at positions >= N in the last block do not take part.
  *
- * q [B][Hq][N][d], k and v [B][Hkv][N][d], o [B][Hq][N][d]: bf16 (uint16 bits)
+ * q [B][Hq][N][d], k [B][Hkv][N][d], o [B][Hq][N][d]: bf16 (uint16 bits)
  * device tensors addressed by the strides; query head h reads KV head
- * h / (Hq / Hkv).  o must not alias q, k or v.  lse (float32 [B*Hq][N],
+ * h / (Hq / Hkv).  v is bf16 in the layout v_layout names: BSA_V_DIM_MAJOR
+ * (the fast path; dim-row stride v_str[2] >= ceil(N/block)*block, key columns
+ * N.. of each row must hold finite values, e.g. the zeros bsa_transpose_rows
+ * writes; per-head byte extents of q, k and v must stay below 2^31) or
+ * BSA_V_TOKEN_MAJOR.  o must not alias q, k or v.  lse (float32 [B*Hq][N],
  * contiguous, device, optional) receives ln(sum_j exp(l_ij + log w_j)) of
  * every query.  row_ptr/col/lw: CSR as built above (lw optional).  order
  * (optional, int32 [R]): launch index -> row; rows not listed are not
@@ -180,6 +203,7 @@ typedef struct {
   const int32_t *scatter_perm_q;
   float scale;
   int32_t causal;
+  int32_t v_layout; /* BSA_V_TOKEN_MAJOR or BSA_V_DIM_MAJOR */
 } bsa_attn_args;
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);

@@ -73,6 +73,13 @@ def test_perm_argument_errors(L):
     assert L.bsa_permute_rows(ctypes.c_void_p(4100), ctypes.c_void_p(8192), FAKE, 1, 1, 8, 128, st, st,
                               None) == _lib.BSA_ERR_ARG
     assert L.bsa_unpermute_rows(FAKE, FAKE, FAKE, 1, 1, 8, 128, st, st, None) == _lib.BSA_ERR_ARG
+    dst = _lib.I64x3(128 * 64, 128 * 64, 64)
+    D2 = ctypes.c_void_p(1 << 20)
+    assert L.bsa_transpose_rows(FAKE, D2, None, 1, 1, 60, 128, 56, st, dst, None) == _lib.BSA_ERR_ARG   # ld < N
+    assert L.bsa_transpose_rows(FAKE, D2, None, 1, 1, 60, 128, 62, st, dst, None) == _lib.BSA_ERR_ARG   # ld % 8
+    assert L.bsa_transpose_rows(FAKE, D2, None, 1, 1, 60, 128, 128, st, dst, None) == _lib.BSA_ERR_ARG  # ld > row
+    assert L.bsa_transpose_rows(FAKE, D2, None, 1, 1, 60, 96, 64, st, dst, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_transpose_rows(FAKE, FAKE, None, 1, 1, 60, 128, 64, st, dst, None) == _lib.BSA_ERR_ARG
 
 
 def test_schedule_argument_errors(L):
@@ -107,6 +114,10 @@ def _args(**kw):
     (dict(o=FAKE), _lib.BSA_ERR_ARG),
     (dict(order=FAKE, n_order=10 ** 6), _lib.BSA_ERR_ARG),
     (dict(N=1 << 40), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(v_layout=2), _lib.BSA_ERR_ARG),
+    (dict(v_layout=1, v_str=_lib.I64x3(128 * 1000, 128 * 1000, 1000)), _lib.BSA_ERR_ARG),   # rows < 1024 keys
+    (dict(v_layout=1, N=1 << 21, q_str=_lib.I64x3(0, 0, 1024), v_str=_lib.I64x3(0, 0, 1 << 21)),
+     _lib.BSA_ERR_UNSUPPORTED),                                                              # 32-bit offsets
 ])
 def test_attn_argument_errors(L, kw, code):
     a = _args(**kw)

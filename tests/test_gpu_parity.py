@@ -51,11 +51,12 @@ def test_csr_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("sched,fuse", [(True, True), (False, False)])
-def test_attention_matches_oracle(name, sched, fuse):
+@pytest.mark.parametrize("sched,fuse,vdm", [(True, True, True), (False, False, True), (True, True, False),
+                                            (False, False, False)])
+def test_attention_matches_oracle(name, sched, fuse, vdm):
     w = make(name)
-    _log("case %s: attention sched=%s fuse=%s" % (name, sched, fuse))
-    _, res = run_gpu(w, schedule=sched, fuse_scatter=fuse, n_xcd=8, wave_rows=16)
+    _log("case %s: attention sched=%s fuse=%s v_dim_major=%s" % (name, sched, fuse, vdm))
+    _, res = run_gpu(w, schedule=sched, fuse_scatter=fuse, n_xcd=8, wave_rows=16, v_dim_major=vdm)
     pq, pk = oracle_perms(w)
     rows = np.arange(w.B * w.Hq * w.N, dtype=np.int64)
     stats = compare_rows(w, res, rows, pq, pk)
@@ -73,12 +74,13 @@ def test_tiny_config_full():
     assert_within(stats)
 
 
-def test_order_invariance_and_determinism():
+@pytest.mark.parametrize("vdm", [True, False])
+def test_order_invariance_and_determinism(vdm):
     w = make("b128_d128_perm_lw")
-    _log("case determinism")
-    _, r1 = run_gpu(w, schedule=False, fuse_scatter=True)
-    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True)
-    _, r3 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False)
+    _log("case determinism v_dim_major=%s" % vdm)
+    _, r1 = run_gpu(w, schedule=False, fuse_scatter=True, v_dim_major=vdm)
+    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True, v_dim_major=vdm)
+    _, r3 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, v_dim_major=vdm)
     a = r1.out.cpu().numpy()
     assert np.array_equal(a, r2.out.cpu().numpy())
     assert np.array_equal(a, r3.out.cpu().numpy())
@@ -99,6 +101,12 @@ def test_perm_and_row_gather_bit_exact():
                                   np.take_along_axis(x, got.reshape(2, 3, 3001)[..., None], 2))
     z = api.unpermute_rows(y, perm)
     np.testing.assert_array_equal(z.cpu().numpy(), xt.cpu().numpy())
+    # gather + transpose into the dim-major layout, zero columns past N
+    for pp in (perm, None):
+        vt = api.transpose_rows(xt, pp, ld=3072).cpu().numpy().view(np.uint16)
+        g = np.take_along_axis(x, got.reshape(2, 3, 3001)[..., None], 2) if pp is not None else x
+        np.testing.assert_array_equal(vt[..., :3001], np.swapaxes(g, 2, 3))
+        assert np.all(vt[..., 3001:] == 0)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,nQB,W,n_xcd", [(1, 4, 4, 37, 8, 1), (2, 8, 2, 20, 16, 8),
