@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: one step = one pass of the whole block-sparse attention path
-(threshold map -> CSR, cluster labels -> permutations, Q/K/V gather, row
-schedule, attention forward with fused scatter-back) on a synthetic
+(threshold map -> CSR, cluster labels -> permutations, Q/K gather, V gather
+into the dim-major layout, row schedule, attention forward with fused
+scatter-back) on a synthetic
 Wan2.1-14B-shaped 720p video DiT self-attention (1 x 40 heads x 75600 tokens,
 d = 128, 128x128 blocks, 64 Gaussian clusters per head, KV blocks kept to
 cumulative mass 0.9, ~15 % density).
@@ -148,13 +149,32 @@ def main():
         "stages_ms": stages,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
-                     "kernel": "attn_fwd_kernel<128,128>",
+                     "traffic": traffic_bytes(args.config),
+                     "traffic_unit": "HBM-side bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                     "kernel": "attn_dimv_128_128",
                      "per_unit": "4*d = 512 FLOP per allowed query-key pair",
                      "units_per_launch": pairs},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def traffic_bytes(cfg):
+    """Bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or None
+    when that summary is for another workload or for other kernel sources."""
+    import hashlib
+    if cfg != "clustered":
+        return None
+    path = os.path.join(ROOT, "profiles", "attn_dimv_wan14b_clustered_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("attn_dimv.hip", "attn_common.h", "attn_fwd.hip"):
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_mask_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def workload_name(cfg):
@@ -176,21 +196,21 @@ def stage_times(pipeline, dw, args, torch):
     ev[0].record(s)
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
     ev[1].record(s)
-    q, k, v, pq = dw.q, dw.k, dw.v, None
+    q, k, pq, pk = dw.q, dw.k, None, None
     if dw.permuted:
         pq = api.perm_from_labels(dw.labels_q, dw.n_clusters)
         pk = api.perm_from_labels(dw.labels_k, dw.n_clusters)
         q = api.permute_rows(dw.q, pq)
         k = api.permute_rows(dw.k, pk)
-        v = api.permute_rows(dw.v, pk)
+    v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
     ev[2].record(s)
     order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd)
     ev[3].record(s)
     api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
-                 causal=dw.causal)
+                 causal=dw.causal, v_dim_major=True)
     ev[4].record(s)
     torch.cuda.synchronize()
-    names = ["mask_to_csr", "perm_and_gather", "schedule", "attention_fused_scatter"]
+    names = ["mask_to_csr", "perm_gather_and_v_transpose", "schedule", "attention_fused_scatter"]
     return {n: round(ev[i].elapsed_time(ev[i + 1]), 4) for i, n in enumerate(names)}
 
 

@@ -57,7 +57,7 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libbsattn.so is not built (run __graft_entry__.build() or "
                                "python block_sparse_attention_mask_amd/build.py)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)   # unresolved symbols fail here
         L.bsa_version.restype = ctypes.c_int
         L.bsa_version.argtypes = []
         L.bsa_strerror.restype = ctypes.c_char_p

@@ -35,6 +35,10 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    # every symbol must resolve (a kernel whose host launch stub was not
+    # emitted shows up here, not on the first GPU call)
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIB)
     return LIB
 

@@ -10,44 +10,40 @@
 //   * 2*BLK/32 wavefronts, two per SIMD.  Wavefront w owns the 32 queries of
 //     group w % (BLK/32) and the key half w / (BLK/32) of every KV tile; the
 //     two halves keep separate online-softmax states that are merged once
-//     through LDS after the last tile.  Two resident wavefronts per SIMD let
-//     one issue MFMAs while the other runs its softmax.
+//     through LDS after the last tile.
 //   * K tiles ([key][dim]) and V^T tiles ([dim][key], V stored dim-major in
-//     HBM) are copied straight into LDS with buffer_load_dwordx4 ... lds:
-//     no register staging, and rows past the end of a buffer come back as
-//     zeros (buffer range checking), so there are no branches on loads.
-//     Two LDS stages: tile e+1 streams in while tile e is computed.
+//     HBM) are copied straight into LDS with buffer_load_dwordx4 ... lds.
+//     Every LDS row is padded by one 16-byte slot, so 16 consecutive rows
+//     start in 16 different bank groups (conflict-free 16-byte reads with
+//     plain immediate offsets); the copy writes junk into the pad slots.
+//     Source offsets are per-lane constants plus a per-tile scalar offset;
+//     rows past the end of a buffer come back as zeros (range checking).
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16.  MFMA row m
 //     of an S^T tile is mapped to key 16(m>>4) + 8((m>>2)&1) + 4((m>>3)&1) +
-//     (m&3), which makes the eight probabilities a lane holds per PV k-step
-//     eight consecutive keys; the matching V^T operand is then one 16-byte LDS
-//     read, as is every K operand.
-//   * LDS rows are 16-byte-chunk XOR-swizzled; the DMA source addresses carry
-//     the inverse swizzle, so reads of 16 consecutive rows hit distinct banks.
+//     (m&3), so that the eight probabilities a lane holds per PV k-step are
+//     eight consecutive keys and the matching V^T operand is one 16-byte read.
+//   * Software pipeline, one barrier per tile: interval i computes
+//     S(i+1) = K(i+1) Q^T in the same basic block as the exponentials of S(i)
+//     (independent, so MFMA and VALU work interleave), then O += V(i) P(i).
+//     K tiles and V tiles each rotate through two LDS stages, one tile apart:
+//     during interval i the copies of K(i+2) and V(i+1) are in flight.
 //   * Softmax in base 2, fp32; the running max is only raised (and O
 //     rescaled) when a tile's max exceeds it by more than 8, which is exact
 //     and leaves probabilities <= 2^8.
 #include "attn_common.h"
 
 namespace bsa {
-namespace {
+namespace dimv {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every num_records used here
-constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOOR = 0x40000000u;     // offset past every buffer (extents < 2^30 bytes)
+constexpr float kTau = 8.0f;               // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
-// 16-byte-chunk swizzle of an LDS row with CPR chunks.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-  return CPR == 16 ? (row & 15) : ((row >> 1) & 7);
 }
 
 // Key (within a 32-key M tile) held by MFMA row m of S^T.
@@ -59,43 +55,42 @@ template <int BLK, int D>
 struct DCfg {
   static constexpr int NQG = BLK / 32;            // query groups of 32
   static constexpr int NW = 2 * NQG;              // wavefronts: query group x key half
-  static constexpr int NT = 64 * NW;              // threads
+  static constexpr int NT = 64 * NW;              // threads (= 4 BLK, the launch bound)
+  static_assert(NT == 4 * BLK, "launch bound");
   static constexpr int MTW = BLK / 64;            // 32-key M tiles per wavefront per KV tile
   static constexpr int KS = D / 16;               // k-steps of K Q^T
   static constexpr int DT = D / 32;               // 32-dim M tiles of O^T
-  static constexpr int KCPR = D / 8;              // 16-byte chunks per K row
-  static constexpr int VCPR = BLK / 8;            // 16-byte chunks per V^T row
-  static constexpr int TILE = BLK * D * 2;        // bytes of one K tile (= one V^T tile)
-  static constexpr int DMA_PER_WAVE = TILE / 1024 / NW;
-  static constexpr int K_ROWS_PER_DMA = 1024 / (D * 2);
-  static constexpr int V_ROWS_PER_DMA = 1024 / (BLK * 2);
-  static constexpr int MERGE_FLOATS = 64 * (DT * 16 + 2);   // per query group
-  static constexpr int BUF = TILE > MERGE_FLOATS * 4 ? TILE : MERGE_FLOATS * 4;   // bytes per LDS buffer
+  static constexpr int KC = D / 8, KP = KC + 1;   // K rows: 16-byte chunks, padded pitch
+  static constexpr int VC = BLK / 8, VP = VC + 1; // V^T rows: chunks, padded pitch
+  static constexpr int NIK = BLK * KP / 64;       // 1 KB copies per K tile
+  static constexpr int NIV = D * VP / 64;         // 1 KB copies per V^T tile
+  static constexpr int NIKW = (NIK + NW - 1) / NW;
+  static constexpr int NIVW = (NIV + NW - 1) / NW;
+  static constexpr int MERGE_FLOATS = 64 * (DT * 16 + 2);  // per query group
+  static constexpr int KBUF = NIK * 1024 > MERGE_FLOATS * 4 ? NIK * 1024 : MERGE_FLOATS * 4;
+  static constexpr int VBUF = NIV * 1024 > MERGE_FLOATS * 4 ? NIV * 1024 : MERGE_FLOATS * 4;
   static constexpr int LIST = 1024;               // CSR entries staged in LDS at a time
-  static_assert(DMA_PER_WAVE * NW * 1024 == TILE, "tile split");
+  static_assert(BLK * KP % 64 == 0 && D * VP % 64 == 0, "whole copies per tile");
   static_assert(NQG <= 4, "one merge buffer per query group");
 };
 
 template <int BLK, int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(DCfg<BLK, D>::NT, DCfg<BLK, D>::NT),
-                          amdgpu_waves_per_eu(2, 2)))
-void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
-                      const int32_t *__restrict__ col, const float *__restrict__ lw,
-                      const int32_t *__restrict__ order, const int32_t *__restrict__ sperm,
-                      uint16_t *__restrict__ out, float *__restrict__ lse) {
+__device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_t *__restrict__ row_ptr,
+                                               const int32_t *__restrict__ col, const float *__restrict__ lw,
+                                               const int32_t *__restrict__ order,
+                                               const int32_t *__restrict__ sperm, uint16_t *__restrict__ out,
+                                               float *__restrict__ lse) {
   // The index arrays are read-only and never alias the outputs (restrict), so
-  // their wave-uniform reads become scalar loads that do not share the vector
-  // memory counter with the in-flight tile copies.
+  // their wave-uniform reads become scalar loads.
   using C = DCfg<BLK, D>;
-  // two LDS stages; separate objects so that the compiler can tell the stage
-  // being filled by DMA from the stage being read
-  __shared__ __attribute__((aligned(1024))) uint8_t k0[C::BUF], v0[C::BUF], k1[C::BUF], v1[C::BUF];
-  // the row's KV-block list and log-weights, staged so that the loop reads
-  // them from LDS instead of waiting on memory
+  // K and V^T stages are separate objects, so the compiler can tell the
+  // stage being filled by DMA from the stages being read.
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[C::KBUF], k1[C::KBUF], v0[C::VBUF], v1[C::VBUF];
   __shared__ int32_t lcol[C::LIST];
   __shared__ float lbias[C::LIST];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hf = lane >> 5;
   const int qg = wave % C::NQG, kh = wave / C::NQG;
   const int32_t r = order ? order[blockIdx.x] : (int32_t)blockIdx.x;
@@ -112,41 +107,78 @@ void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
   const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((N - 1) * p.qs2 + D) * 2);
   const rsrc_t krs = make_rsrc(p.k + b * p.ks0 + g * p.ks1, ((N - 1) * p.ks2 + D) * 2);
   const rsrc_t vrs = make_rsrc(p.v + b * p.vs0 + g * p.vs1, (int64_t)D * p.vs2 * 2);
+  const uint32_t ks2b = (uint32_t)p.ks2 * 2, vs2b = (uint32_t)p.vs2 * 2;
 
   // Q^T fragment (B operand): lane (ln, hf) holds q[qi][16 ks + 8 hf .. +7]
   bf16x8 qf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    const uint32_t off = qi < N ? (uint32_t)((qi * p.qs2 + ks * 16 + hf * 8) * 2) : kOutOfRange;
+    const uint32_t off = qi < N ? (uint32_t)((qi * p.qs2 + ks * 16 + hf * 8) * 2) : kOOR;
     qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   }
 
-  // Stream tile e (its K rows and V^T rows) into LDS stage `st`.
-  const uint32_t ks2b = (uint32_t)p.ks2 * 2, vs2b = (uint32_t)p.vs2 * 2;
-  const int32_t n32 = (int32_t)(N < INT32_MAX ? N : INT32_MAX);
-  auto issue_tile = [&](int i, uint8_t *kdst, uint8_t *vdst) {
-    // an out-of-range block index reads nothing (all rows out of range)
-    const uint32_t vb = (uint32_t)lcol[i];
-    const int32_t key0 = (int32_t)((vb < (uint32_t)p.nQB ? vb : (uint32_t)p.nQB) * BLK);
-    const bool inside = vb < (uint32_t)p.nQB;
+  // Per-lane source offsets of this wavefront's 1 KB copies (copy I = wave + NW t
+  // writes LDS slots 64 I .. 64 I + 63, slot s = row * pitch + chunk).
+  uint32_t kvo[C::NIKW], vvo[C::NIVW];
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const int I = wave * C::DMA_PER_WAVE + i;
-      {
-        const int row = I * C::K_ROWS_PER_DMA + lane / C::KCPR;
-        const int cc = (lane % C::KCPR) ^ swz<C::KCPR>(row);
-        const int32_t key = key0 + row;
-        const uint32_t off0 = (uint32_t)(key < n32 ? key : 0) * ks2b + cc * 16;
-        const uint32_t off = key < n32 ? off0 : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(kdst + I * 1024), 16, off, 0, 0, 0);
-      }
-      {
-        const int row = I * C::V_ROWS_PER_DMA + lane / C::VCPR;   // head-dim row
-        const int cc = (lane % C::VCPR) ^ swz<C::VCPR>(row);
-        const uint32_t off = inside ? (uint32_t)row * vs2b + (uint32_t)key0 * 2 + cc * 16 : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(vdst + I * 1024), 16, off, 0, 0, 0);
-      }
+  for (int t = 0; t < C::NIKW; ++t) {
+    const int s = (wave + C::NW * t) * 64 + lane;
+    const int row = s / C::KP, c = s % C::KP;
+    kvo[t] = (c < C::KC && row < BLK) ? (uint32_t)row * ks2b + c * 16 : kOOR;
+  }
+#pragma unroll
+  for (int t = 0; t < C::NIVW; ++t) {
+    const int s = (wave + C::NW * t) * 64 + lane;
+    const int row = s / C::VP, c = s % C::VP;
+    vvo[t] = (c < C::VC && row < D) ? (uint32_t)row * vs2b + c * 16 : kOOR;
+  }
+  // scalar offset of list entry i's tile, or one past every buffer for a
+  // block index outside the rows (then the tile reads as zeros)
+  auto k_soff = [&](int i) -> uint32_t {
+    const uint32_t vb = (uint32_t)lcol[i];
+    return vb < (uint32_t)p.nQB ? vb * BLK * ks2b : kOOR;   // rows >= N read as zeros
+  };
+  auto v_soff = [&](int i) -> uint32_t {
+    const uint32_t vb = (uint32_t)lcol[i];
+    return vb < (uint32_t)p.nQB ? vb * BLK * 2 : kOOR;
+  };
+  auto issue_k = [&](int i, uint8_t *dst) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(k_soff(i));
+#pragma unroll
+    for (int t = 0; t < C::NIKW; ++t) {
+      const int I = wave + C::NW * t;
+      if (I < C::NIK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(dst + I * 1024), 16, kvo[t], so, 0, 0);
     }
+  };
+  auto issue_v = [&](int i, uint8_t *dst) {
+    const uint32_t so = __builtin_amdgcn_readfirstlane(v_soff(i));
+#pragma unroll
+    for (int t = 0; t < C::NIVW; ++t) {
+      const int I = wave + C::NW * t;
+      if (I < C::NIV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(dst + I * 1024), 16, vvo[t], so, 0, 0);
+    }
+  };
+
+  // LDS read bases (immediate offsets do the rest)
+  int kb[C::MTW];
+#pragma unroll
+  for (int jj = 0; jj < C::MTW; ++jj) kb[jj] = (32 * (kh * C::MTW + jj) + key_of_row(ln)) * C::KP * 16 + hf * 16;
+  const int vbase = ln * C::VP * 16 + hf * 16;
+
+  auto qk = [&](f32x16 (&s)[C::MTW], const uint8_t *kt) {
+#pragma unroll
+    for (int jj = 0; jj < C::MTW; ++jj)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[jj][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < C::MTW; ++jj) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(kt + kb[jj] + ks * 32);
+        s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[jj], 0, 0, 0);
+      }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -155,85 +187,77 @@ void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  f32x16 sa[C::MTW], sb[C::MTW];
 
-  auto compute_tile = [&](int i, const uint8_t *kt, const uint8_t *vt) {
-      const int64_t vblk = (int64_t)(uint32_t)lcol[i];
-      const float bias = lbias[i];
-
-      // S^T = K Q^T for this wavefront's BLK/2 keys
-      f32x16 s[C::MTW];
+  // One pipeline interval: softmax of S(i) (in sc) overlapped with
+  // S(i+1) = K(i+1) Q^T (into sn), then O += V(i) P(i).
+  auto interval = [&](int i, f32x16 (&sc)[C::MTW], f32x16 (&sn)[C::MTW], const uint8_t *kt_next,
+                      const uint8_t *vt) {
+    const int64_t vblk = (int64_t)(uint32_t)lcol[i];
+    const float bias = lbias[i];
+    // keys past N (last block) and, when causal, keys after the query
+    const int64_t kbase = vblk * BLK;
+    if (kbase + BLK > N || (p.causal && vblk >= u)) {
+      const int64_t ln_ = N - kbase;
+      const int lim_n = ln_ < 0 ? 0 : (ln_ > BLK ? BLK : (int)ln_);   // offsets >= lim_n are padding
+      const int64_t lc_ = p.causal ? qi - kbase : (int64_t)BLK;
+      const int lim_c = lc_ < -1 ? -1 : (lc_ > BLK ? BLK : (int)lc_);  // offsets > lim_c are masked
 #pragma unroll
       for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[jj][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int jj = 0; jj < C::MTW; ++jj) {
-          const int row = 32 * (kh * C::MTW + jj) + key_of_row(ln);
-          const int ch = (2 * ks + hf) ^ swz<C::KCPR>(row);
-          const uint4 a = *reinterpret_cast<const uint4 *>(kt + row * (D * 2) + ch * 16);
-          s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[jj], 0, 0, 0);
+        for (int e = 0; e < 16; ++e) {
+          const int off = 32 * (kh * C::MTW + jj) + 16 * (e >> 3) + 8 * hf + (e & 7);
+          if (off >= lim_n || off > lim_c) sc[jj][e] = -INFINITY;
         }
-      }
-
-      // keys past N (last block) and, when causal, keys after the query
-      const int64_t kbase = vblk * BLK;
-      if (kbase + BLK > N || (p.causal && vblk >= u)) {
-        const int64_t ln_ = N - kbase;
-        const int lim_n = ln_ < 0 ? 0 : (ln_ > BLK ? BLK : (int)ln_);   // offsets >= lim_n are padding
-        const int64_t lc_ = p.causal ? qi - kbase : (int64_t)BLK;
-        const int lim_c = lc_ < -1 ? -1 : (lc_ > BLK ? BLK : (int)lc_);  // offsets > lim_c are masked
+    }
+    float mx = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < C::MTW; ++jj)
+    for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = 32 * (kh * C::MTW + jj) + 16 * (i >> 3) + 8 * hf + (i & 7);
-            if (off >= lim_n || off > lim_c) s[jj][i] = -INFINITY;
-          }
-      }
-
-      float mx = -INFINITY;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[jj][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = (mx == -INFINITY) ? -INFINITY : fmaf(mx, p.c, bias);
+    if (__any(m_tile > m_run + kTau)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      m_run = m_new;
+    }
+    const float nb = bias - (m_run == -INFINITY ? 0.f : m_run);
+    bf16x8 pb[C::MTW][2];
+    auto exps = [&]() {
 #pragma unroll
       for (int jj = 0; jj < C::MTW; ++jj)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[jj][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = (mx == -INFINITY) ? -INFINITY : fmaf(mx, p.c, bias);
-      if (__any(m_tile > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      const float nb = bias - (m_run == -INFINITY ? 0.f : m_run);
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int jj = 0; jj < C::MTW; ++jj) {
-        const int j = kh * C::MTW + jj;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           float pv[8];
 #pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
+          for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(sc[jj][8 * s2 + e8], p.c, nb));
           l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-          const uint4 pk = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                                      cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) {
-            const int row = 32 * dt + ln;
-            const int ch = (4 * j + 2 * s2 + hf) ^ swz<C::VCPR>(row);
-            const uint4 a = *reinterpret_cast<const uint4 *>(vt + row * (BLK * 2) + ch * 16);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt], 0, 0, 0);
-          }
+          pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                                                             cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
         }
-      }
+    };
+    // S(i+1) is computed unconditionally so that the MFMAs and the
+    // exponentials share one basic block; after a row's last tile it reads a
+    // stale stage and is never used
+    qk(sn, kt_next);
+    exps();
+#pragma unroll
+    for (int jj = 0; jj < C::MTW; ++jj) {
+      const int j = kh * C::MTW + jj;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(vt + vbase + dt * 32 * C::VP * 16 + (4 * j + 2 * s2) * 16);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj][s2], o[dt], 0, 0, 0);
+        }
+    }
   };
 
   for (int c0 = e0; c0 < e1; c0 += C::LIST) {
@@ -243,17 +267,25 @@ void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
       lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
     }
     __syncthreads();
-    issue_tile(0, k0, v0);
+    // prologue: K(0), V(0), K(1) resident, then S(0)
+    issue_k(0, k0);
+    issue_v(0, v0);
+    if (n > 1) issue_k(1, k1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    qk(sa, k0);
     for (int i = 0; i < n; i += 2) {
-      if (i + 1 < n) issue_tile(i + 1, k1, v1);
-      compute_tile(i, k0, v0);
-      __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of tile i+1 have landed
-      __syncthreads();                 // ... and everyone else's; stage 0 is free again
+      // interval i (even): reads K(i+1) in k1, V(i) in v0; fills k0 <- K(i+2), v1 <- V(i+1)
+      if (i + 2 < n) issue_k(i + 2, k0);
+      if (i + 1 < n) issue_v(i + 1, v1);
+      interval(i, sa, sb, k1, v0);
+      __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies have landed
+      __syncthreads();                 // ... and everyone's; the stages read above are free
       if (i + 1 >= n) break;
-      if (i + 2 < n) issue_tile(i + 2, k0, v0);
-      compute_tile(i + 1, k1, v1);
+      // interval i+1 (odd): reads K(i+2) in k0, V(i+1) in v1; fills k1 <- K(i+3), v0 <- V(i+2)
+      if (i + 3 < n) issue_k(i + 3, k1);
+      if (i + 2 < n) issue_v(i + 2, v0);
+      interval(i + 1, sb, sa, k0, v1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -262,7 +294,8 @@ void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
   // merge the two key halves of every query group, normalise, store
   const float l_w = l_run + __shfl_xor(l_run, 32);
   // after the last barrier no tile is read any more: one buffer per query group
-  float *scratch = reinterpret_cast<float *>(qg == 0 ? k0 : qg == 1 ? v0 : qg == 2 ? k1 : v1);
+  uint8_t *const mbuf = qg == 0 ? (uint8_t *)k0 : qg == 1 ? (uint8_t *)v0 : qg == 2 ? (uint8_t *)k1 : (uint8_t *)v1;
+  float *scratch = reinterpret_cast<float *>(mbuf);
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -301,19 +334,31 @@ void attn_dimv_kernel(const AttnParams p, const int32_t *__restrict__ row_ptr,
   }
 }
 
-template <int BLK, int D>
-void launch_one(const AttnParams &p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_dimv_kernel<BLK, D>), dim3((unsigned)grid), dim3(DCfg<BLK, D>::NT), 0, s, p,
-                     p.row_ptr, p.col, p.lw, p.order, p.sperm, p.o, p.lse);
-}
+// One plain kernel per tile shape (the body is a force-inlined template).
+#define BSA_DIMV_KERNEL(BLK, D)                                                                     \
+  __global__ __attribute__((amdgpu_flat_work_group_size(4 * BLK, 4 * BLK), amdgpu_waves_per_eu(2, 2))) \
+  void attn_dimv_##BLK##_##D(const AttnParams p, const int32_t *__restrict__ row_ptr,              \
+                             const int32_t *__restrict__ col, const float *__restrict__ lw,          \
+                             const int32_t *__restrict__ order, const int32_t *__restrict__ sperm,   \
+                             uint16_t *__restrict__ out, float *__restrict__ lse) {                  \
+    attn_dimv_body<BLK, D>(p, row_ptr, col, lw, order, sperm, out, lse);                           \
+  }
+BSA_DIMV_KERNEL(128, 128)
+BSA_DIMV_KERNEL(128, 64)
+BSA_DIMV_KERNEL(64, 128)
+BSA_DIMV_KERNEL(64, 64)
+#undef BSA_DIMV_KERNEL
 
-}  // namespace
+}  // namespace dimv
 
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s) {
-  if (block == 128 && d == 128) launch_one<128, 128>(p, grid, s);
-  else if (block == 128) launch_one<128, 64>(p, grid, s);
-  else if (d == 128) launch_one<64, 128>(p, grid, s);
-  else launch_one<64, 64>(p, grid, s);
+  const dim3 g((unsigned)grid), t(4 * block);
+#define BSA_ARGS p, p.row_ptr, p.col, p.lw, p.order, p.sperm, p.o, p.lse
+  if (block == 128 && d == 128) hipLaunchKernelGGL(dimv::attn_dimv_128_128, g, t, 0, s, BSA_ARGS);
+  else if (block == 128) hipLaunchKernelGGL(dimv::attn_dimv_128_64, g, t, 0, s, BSA_ARGS);
+  else if (d == 128) hipLaunchKernelGGL(dimv::attn_dimv_64_128, g, t, 0, s, BSA_ARGS);
+  else hipLaunchKernelGGL(dimv::attn_dimv_64_64, g, t, 0, s, BSA_ARGS);
+#undef BSA_ARGS
   return hipGetLastError();
 }
 

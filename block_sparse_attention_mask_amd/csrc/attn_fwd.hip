@@ -29,10 +29,10 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   const int64_t nQB = (a->N + a->block - 1) / a->block;
   const int64_t R = (int64_t)a->B * a->Hq * nQB;
   if (R >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
-  const int64_t lim = int64_t(1) << 31;
+  const int64_t lim = int64_t(1) << 30;
   if (a->v_layout == BSA_V_DIM_MAJOR) {
     // rows of V^T must hold every key of the last block; per-head byte ranges
-    // are addressed with 32-bit buffer offsets
+    // are addressed with buffer offsets below 2^30
     if (a->v_str[2] < nQB * a->block) return BSA_ERR_ARG;
     if (((a->N - 1) * a->q_str[2] + a->d) * 2 >= lim || ((a->N - 1) * a->k_str[2] + a->d) * 2 >= lim ||
         (int64_t)a->d * a->v_str[2] * 2 >= lim)

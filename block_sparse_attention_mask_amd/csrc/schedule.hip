@@ -94,14 +94,10 @@ extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32
   if (wave_rows > kMaxWave) return BSA_ERR_UNSUPPORTED;
   const int64_t R = (int64_t)B * Hq * nQB;
   if (R >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
-  int W = wave_rows;
-  if (W == 0) {
-    int cus = bsa_device_cus();
-    if (cus < 0) return cus;
-    W = cus / (n_xcd > 1 ? n_xcd : 1);
-    if (W < 1) W = 1;
-    if (W > kMaxWave) W = kMaxWave;
-  }
+  // wave_rows = 0: one bucket per KV-group segment (up to 2048 rows), i.e. the
+  // whole head longest-first, which measured fastest on MI355X together with
+  // the XCD-contiguous deal
+  const int W = wave_rows ? wave_rows : kMaxWave;
   const int64_t seg = (int64_t)(Hq / Hkv) * nQB;
   const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),

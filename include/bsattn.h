@@ -155,8 +155,9 @@ int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t 
  * ascending).  When n_xcd > 1 the list is dealt to launch indices so that the
  * GPU's round-robin dispatch gives XCD x the x-th contiguous slice:
  * order[i] = logical[start(i % n_xcd) + i / n_xcd].  wave_rows = 0 selects
- * (compute units / max(1, n_xcd)).  row_ptr: device int32 [R+1];
- * order: device int32 [R] (output).  wave_rows <= 2048.  Asynchronous.
+ * 2048 (a whole segment of up to 2048 rows is one bucket).  row_ptr: device
+ * int32 [R+1]; order: device int32 [R] (output).  wave_rows <= 2048.
+ * Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
                  int32_t wave_rows, int32_t n_xcd, int32_t *order, bsa_stream_t stream);
@@ -178,7 +179,7 @@ int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int
  * h / (Hq / Hkv).  v is bf16 in the layout v_layout names: BSA_V_DIM_MAJOR
  * (the fast path; dim-row stride v_str[2] >= ceil(N/block)*block, key columns
  * N.. of each row must hold finite values, e.g. the zeros bsa_transpose_rows
- * writes; per-head byte extents of q, k and v must stay below 2^31) or
+ * writes; per-head byte extents of q, k and v must stay below 2^30) or
  * BSA_V_TOKEN_MAJOR.  o must not alias q, k or v.  lse (float32 [B*Hq][N],
  * contiguous, device, optional) receives ln(sum_j exp(l_ij + log w_j)) of
  * every query.  row_ptr/col/lw: CSR as built above (lw optional).  order

@@ -116,7 +116,7 @@ def _args(**kw):
     (dict(N=1 << 40), _lib.BSA_ERR_UNSUPPORTED),
     (dict(v_layout=2), _lib.BSA_ERR_ARG),
     (dict(v_layout=1, v_str=_lib.I64x3(128 * 1000, 128 * 1000, 1000)), _lib.BSA_ERR_ARG),   # rows < 1024 keys
-    (dict(v_layout=1, N=1 << 21, q_str=_lib.I64x3(0, 0, 1024), v_str=_lib.I64x3(0, 0, 1 << 21)),
+    (dict(v_layout=1, N=1 << 20, q_str=_lib.I64x3(0, 0, 1024), v_str=_lib.I64x3(0, 0, 1 << 20)),
      _lib.BSA_ERR_UNSUPPORTED),                                                              # 32-bit offsets
 ])
 def test_attn_argument_errors(L, kw, code):
