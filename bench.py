@@ -151,7 +151,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config),
                      "traffic_unit": "HBM-side bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
-                     "kernel": "attn_dimv_128_128",
+                     "kernel": attn_kernel_name(w.block, w.d),
                      "per_unit": "4*d = 512 FLOP per allowed query-key pair",
                      "units_per_launch": pairs},
         "cpu_baseline": cpu,
@@ -159,20 +159,32 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def attn_kernel_name(block, d):
+    """The attention kernel bsa_attn_fwd launches for dim-major V."""
+    return ("attn_pp_128_%d" % d) if block == 128 else ("attn_dimv_%d_%d" % (block, d))
+
+
+ATTN_SOURCES = ("attn_pp.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip")
+
+
+def attn_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_sparse_attention_mask_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_bytes(cfg):
     """Bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or None
     when that summary is for another workload or for other kernel sources."""
-    import hashlib
     if cfg != "clustered":
         return None
-    path = os.path.join(ROOT, "profiles", "attn_dimv_wan14b_clustered_traffic.json")
+    path = os.path.join(ROOT, "profiles", "attn_wan14b_clustered_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in ("attn_dimv.hip", "attn_common.h", "attn_fwd.hip"):
-        h.update(open(os.path.join(ROOT, "block_sparse_attention_mask_amd", "csrc", f), "rb").read())
-    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+    if attn_sources_sha256() != rec.get("kernel_sources_sha256"):
         return None
     return int(rec["traffic_bytes_per_launch"])
 

@@ -35,7 +35,37 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOOR = 0x40000000u;     // offset past every buffer (extents < 2^30 bytes)
+constexpr float kTau = 8.0f;               // lazy-rescale threshold (log2 units)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Key (within a 32-key M tile) held by MFMA row m of S^T.
+__device__ __forceinline__ int key_of_row(int m) {
+  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
+}
+
+// Max and sum of a value over lanes l and l ^ 32 (the two halves of a
+// wavefront hold different keys of the same queries).  The swap returns the
+// upper half's value in the first result and the lower half's in the second,
+// in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 hipError_t launch_attn_tokv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
+hipError_t launch_attn_pp(const AttnParams &p, int d, int64_t grid, hipStream_t s);
 
 }  // namespace bsa

@@ -35,22 +35,6 @@
 namespace bsa {
 namespace dimv {
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kOOR = 0x40000000u;     // offset past every buffer (extents < 2^30 bytes)
-constexpr float kTau = 8.0f;               // lazy-rescale threshold (log2 units)
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
-// Key (within a 32-key M tile) held by MFMA row m of S^T.
-__device__ __forceinline__ int key_of_row(int m) {
-  return ((m >> 4) << 4) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2) | (m & 3);
-}
-
 template <int BLK, int D>
 struct DCfg {
   static constexpr int NQG = BLK / 32;            // query groups of 32
@@ -91,6 +75,7 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < C::NW);
   const int ln = lane & 31, hf = lane >> 5;
   const int qg = wave % C::NQG, kh = wave / C::NQG;
   const int32_t r = order ? order[blockIdx.x] : (int32_t)blockIdx.x;
@@ -100,12 +85,17 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   const int64_t b = bh / p.Hq;
   const int h = (int)(bh - b * p.Hq);
   const int g = h / p.G;
-  const int64_t N = p.N;
+  // every per-head extent is below 2^30 bytes, so token positions fit in 32 bits
+  const int N = (int)p.N;
   const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
-  const int64_t qi = (int64_t)u * BLK + qg * 32 + ln;   // this lane's query position
+  // KV blocks at or after mlim need the element mask: the partial last block
+  // and, when causal, blocks from the diagonal on
+  const int nfull = N / BLK;
+  const int mlim = p.causal ? (u < nfull ? u : nfull) : nfull;
+  const int qi = u * BLK + qg * 32 + ln;   // this lane's query position
 
-  const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((N - 1) * p.qs2 + D) * 2);
-  const rsrc_t krs = make_rsrc(p.k + b * p.ks0 + g * p.ks1, ((N - 1) * p.ks2 + D) * 2);
+  const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((int64_t)(N - 1) * p.qs2 + D) * 2);
+  const rsrc_t krs = make_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
   const rsrc_t vrs = make_rsrc(p.v + b * p.vs0 + g * p.vs1, (int64_t)D * p.vs2 * 2);
   const uint32_t ks2b = (uint32_t)p.ks2 * 2, vs2b = (uint32_t)p.vs2 * 2;
 
@@ -113,7 +103,7 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   bf16x8 qf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    const uint32_t off = qi < N ? (uint32_t)((qi * p.qs2 + ks * 16 + hf * 8) * 2) : kOOR;
+    const uint32_t off = qi < N ? (uint32_t)(((int64_t)qi * p.qs2 + ks * 16 + hf * 8) * 2) : kOOR;
     qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   }
 
@@ -142,23 +132,28 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
     const uint32_t vb = (uint32_t)lcol[i];
     return vb < (uint32_t)p.nQB ? vb * BLK * 2 : kOOR;
   };
+  // The LDS destination of copy t is stage + 1024 (wave + NW t); all but the
+  // last copy of every wavefront exist (NW (NIKW - 1) < NIK).  The wave offset
+  // passes through an empty asm so that the per-copy addresses are formed at
+  // each issue (one scalar add each) instead of occupying scalar registers for
+  // the whole loop.
   auto issue_k = [&](int i, uint8_t *dst) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(k_soff(i));
+    int wo = wave * 1024;
+    asm volatile("" : "+s"(wo));
 #pragma unroll
-    for (int t = 0; t < C::NIKW; ++t) {
-      const int I = wave + C::NW * t;
-      if (I < C::NIK)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(dst + I * 1024), 16, kvo[t], so, 0, 0);
-    }
+    for (int t = 0; t < C::NIKW; ++t)
+      if (t < C::NIKW - 1 || wave + C::NW * t < C::NIK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(dst + wo + C::NW * 1024 * t), 16, kvo[t], so, 0, 0);
   };
   auto issue_v = [&](int i, uint8_t *dst) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(v_soff(i));
+    int wo = wave * 1024;
+    asm volatile("" : "+s"(wo));
 #pragma unroll
-    for (int t = 0; t < C::NIVW; ++t) {
-      const int I = wave + C::NW * t;
-      if (I < C::NIV)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(dst + I * 1024), 16, vvo[t], so, 0, 0);
-    }
+    for (int t = 0; t < C::NIVW; ++t)
+      if (t < C::NIVW - 1 || wave + C::NW * t < C::NIV)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(dst + wo + C::NW * 1024 * t), 16, vvo[t], so, 0, 0);
   };
 
   // LDS read bases (immediate offsets do the rest)
@@ -166,6 +161,7 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
 #pragma unroll
   for (int jj = 0; jj < C::MTW; ++jj) kb[jj] = (32 * (kh * C::MTW + jj) + key_of_row(ln)) * C::KP * 16 + hf * 16;
   const int vbase = ln * C::VP * 16 + hf * 16;
+  const int ob = 32 * kh * C::MTW + 8 * hf;   // key offset of this lane's first score row
 
   auto qk = [&](f32x16 (&s)[C::MTW], const uint8_t *kt) {
 #pragma unroll
@@ -193,29 +189,29 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   // S(i+1) = K(i+1) Q^T (into sn), then O += V(i) P(i).
   auto interval = [&](int i, f32x16 (&sc)[C::MTW], f32x16 (&sn)[C::MTW], const uint8_t *kt_next,
                       const uint8_t *vt) {
-    const int64_t vblk = (int64_t)(uint32_t)lcol[i];
+    const uint32_t vb = (uint32_t)lcol[i];
     const float bias = lbias[i];
-    // keys past N (last block) and, when causal, keys after the query
-    const int64_t kbase = vblk * BLK;
-    if (kbase + BLK > N || (p.causal && vblk >= u)) {
-      const int64_t ln_ = N - kbase;
-      const int lim_n = ln_ < 0 ? 0 : (ln_ > BLK ? BLK : (int)ln_);   // offsets >= lim_n are padding
-      const int64_t lc_ = p.causal ? qi - kbase : (int64_t)BLK;
-      const int lim_c = lc_ < -1 ? -1 : (lc_ > BLK ? BLK : (int)lc_);  // offsets > lim_c are masked
+    if (vb >= (uint32_t)mlim) {
+      // keys past N (last block) and, when causal, keys after the query; a
+      // block index outside the rows masks every key.  Element e of M tile
+      // jj holds key offset ob + 32 jj + 16 (e >> 3) + (e & 7) in the block.
+      const int vbc = vb < (uint32_t)p.nQB ? (int)vb : p.nQB;
+      const int kbase = vbc * BLK;
+      const int lim_n = N - kbase > BLK ? BLK : (N - kbase < 0 ? 0 : N - kbase);   // offsets >= lim_n: padding
+      const int lc = p.causal ? qi - kbase + 1 : BLK;                               // offsets >= lc: after the query
+      const int lim = (lc < lim_n ? lc : lim_n) - ob;
 #pragma unroll
       for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = 32 * (kh * C::MTW + jj) + 16 * (e >> 3) + 8 * hf + (e & 7);
-          if (off >= lim_n || off > lim_c) sc[jj][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (32 * jj + 16 * (e >> 3) + (e & 7) >= lim) sc[jj][e] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[jj][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float m_tile = (mx == -INFINITY) ? -INFINITY : fmaf(mx, p.c, bias);
     if (__any(m_tile > m_run + kTau)) {
       const float m_new = fmaxf(m_run, m_tile);
@@ -274,6 +270,9 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(sa, k0);
+    // the first interval refills k0 with K(2): every wavefront must be done
+    // reading K(0) first
+    if (n > 2) __syncthreads();
     for (int i = 0; i < n; i += 2) {
       // interval i (even): reads K(i+1) in k1, V(i) in v0; fills k0 <- K(i+2), v1 <- V(i+1)
       if (i + 2 < n) issue_k(i + 2, k0);
@@ -292,7 +291,7 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   }
 
   // merge the two key halves of every query group, normalise, store
-  const float l_w = l_run + __shfl_xor(l_run, 32);
+  const float l_w = halves_sum(l_run);
   // after the last barrier no tile is read any more: one buffer per query group
   uint8_t *const mbuf = qg == 0 ? (uint8_t *)k0 : qg == 1 ? (uint8_t *)v0 : qg == 2 ? (uint8_t *)k1 : (uint8_t *)v1;
   float *scratch = reinterpret_cast<float *>(mbuf);
@@ -315,9 +314,9 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
   const float l_tot = l_w * a1 + l2 * a2;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t oi = (qi < N && sperm) ? (int64_t)sperm[bh * N + qi] : qi;
+  const int oi = (qi < N && sperm) ? sperm[bh * N + qi] : qi;
   if (qi < N && oi >= 0 && oi < N) {
-    uint16_t *ob = out + b * p.os0 + h * p.os1 + oi * p.os2;
+    uint16_t *ob16 = out + b * p.os0 + h * p.os1 + (int64_t)oi * p.os2;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -327,7 +326,7 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
         const float x1 = (o[dt][4 * i4 + 1] * a1 + o2[1] * a2) * inv;
         const float x2 = (o[dt][4 * i4 + 2] * a1 + o2[2] * a2) * inv;
         const float x3 = (o[dt][4 * i4 + 3] * a1 + o2[3] * a2) * inv;
-        *reinterpret_cast<uint2 *>(ob + 32 * dt + 8 * i4 + 4 * hf) =
+        *reinterpret_cast<uint2 *>(ob16 + 32 * dt + 8 * i4 + 4 * hf) =
             make_uint2(cvt_pk_bf16(x0, x1), cvt_pk_bf16(x2, x3));
       }
     if (lse && hf == 0) lse[bh * N + oi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;

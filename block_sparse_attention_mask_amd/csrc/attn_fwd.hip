@@ -1,5 +1,6 @@
 // bsa_attn_fwd: argument checks and dispatch to the attention kernels
-// (dim-major V: attn_dimv.hip; token-major V: attn_tokv.hip).
+// (dim-major V: attn_pp.hip for 128-key blocks, attn_dimv.hip for 64;
+// token-major V: attn_tokv.hip).
 #include "attn_common.h"
 
 namespace {
@@ -69,7 +70,9 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   p.c = scale * bsa::kLog2e;
 
   hipStream_t s = bsa_hip_stream(stream);
-  const hipError_t err = a->v_layout == BSA_V_DIM_MAJOR ? bsa::launch_attn_dimv(p, a->block, a->d, grid, s)
-                                                        : bsa::launch_attn_tokv(p, a->block, a->d, grid, s);
+  hipError_t err;
+  if (a->v_layout == BSA_V_TOKEN_MAJOR) err = bsa::launch_attn_tokv(p, a->block, a->d, grid, s);
+  else if (a->block == 128) err = bsa::launch_attn_pp(p, a->d, grid, s);
+  else err = bsa::launch_attn_dimv(p, a->block, a->d, grid, s);
   return err == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
