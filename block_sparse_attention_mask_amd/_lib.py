@@ -22,7 +22,7 @@ BSA_V_DIM_MAJOR = 1
 # Every symbol include/bsattn.h declares.
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_schedule", "bsa_attn_fwd",
-           "bsa_device_cus")
+           "bsa_device_cus", "bsa_device_clock_khz")
 
 
 class AttnArgs(ctypes.Structure):
@@ -81,6 +81,8 @@ def load():
         L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
         L.bsa_device_cus.restype = ctypes.c_int
         L.bsa_device_cus.argtypes = []
+        L.bsa_device_clock_khz.restype = ctypes.c_int
+        L.bsa_device_clock_khz.argtypes = []
         _lib = L
     return _lib
 

@@ -56,6 +56,13 @@ def device_cus() -> int:
     return n
 
 
+def device_clock_khz() -> int:
+    k = load().bsa_device_clock_khz()
+    if k < 0:
+        check("bsa_device_clock_khz", k)
+    return k
+
+
 def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,
               row_ptr: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, int]:
     src = mask if mask is not None else T

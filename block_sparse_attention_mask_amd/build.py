@@ -20,13 +20,15 @@ FLAGS = [
 ]
 
 
+# Per-source compiler flags beyond FLAGS (none at present).
+EXTRA: dict = {}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + sources() + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,6 +37,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    tmp = LIB + ".tmp%d" % os.getpid()
+    with tempfile.TemporaryDirectory(prefix="bsattn_build_") as od:
+        objs, cmds = [], []
+        for src in sources():
+            obj = os.path.join(od, os.path.basename(src) + ".o")
+            flags = [f for f in FLAGS if f != "-shared"]
+            cmds.append([HIPCC] + flags + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj])
+            objs.append(obj)
+        with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     # every symbol must resolve (a kernel whose host launch stub was not
     # emitted shows up here, not on the first GPU call)
     import ctypes

@@ -64,6 +64,41 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Chunk-position permutation of LDS row r (rows of `chunks` 16-byte chunks).
+template <int chunks>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(chunks == 8 || chunks == 16, "row width");
+  return chunks == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (SGPR quad) for a byte range starting at base.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+}
+
+// One 1 KB copy: 16 bytes per lane from buffer offset voff (+ soff) into LDS
+// at lds + 16 lane.  Written as inline assembly so that the compiler does not
+// track it (its waits are placed by hand at phase ends): M0 carries the LDS
+// address; the nops cover the M0 and SGPR-operand hazards of a vector memory
+// instruction.  No wavefront reads a buffer in the phase that refills it, and
+// the phase barriers order everything else, so no memory clobber is needed.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rsrc), "s"(soff)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate (gfx9 encoding): at most n vector-memory operations of
+// this wavefront outstanding, no LDS/scalar-memory operation outstanding,
+// export counter not waited on.
+constexpr int vm_lgkm0_wait_imm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+
 hipError_t launch_attn_tokv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_pp(const AttnParams &p, int d, int64_t grid, hipStream_t s);

@@ -164,3 +164,10 @@ extern "C" int bsa_device_cus(void) {
     return BSA_ERR_HIP;
   return n;
 }
+
+extern "C" int bsa_device_clock_khz(void) {
+  int dev = 0, k = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BSA_ERR_HIP;
+  if (hipDeviceGetAttribute(&k, hipDeviceAttributeClockRate, dev) != hipSuccess) return BSA_ERR_HIP;
+  return k;
+}

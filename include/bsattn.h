@@ -213,6 +213,10 @@ int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);
  * negative error. */
 int bsa_device_cus(void);
 
+/* Peak engine clock of the current device in kHz (for reporting the clock a
+ * measurement ran under), or a negative error. */
+int bsa_device_clock_khz(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from block_sparse_attention_mask_amd import api, pipeline, synth
-from parity_common import (assert_within, bf16_tensor_to_f32, compare_rows, oracle_csr, oracle_perms,
+from parity_common import (assert_within, bf16_tensor_to_f32, compare_rows, oracle_csr, oracle_perms, sample_rows,
                            run_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +145,21 @@ def test_zero_queries_and_constant_values():
     # P is rounded to bf16 for the PV product while the row sum uses fp32 P, so
     # a constant V comes back within one bf16 ulp (2^-8 at 0.625), not exactly
     assert np.abs(bf16_tensor_to_f32(res.out) - np.float32(0.625)).max() <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("block,d,nblocks", [(128, 128, 1100), (64, 64, 1100)])
+def test_long_rows_span_list_chunks(block, d, nblocks):
+    """Rows of over a thousand KV blocks: the kernels stage a row's CSR list in
+    LDS in chunks, so these rows cross chunk boundaries (online-softmax state
+    carried across chunks).  Sampled rows: one random query block per head and
+    the tail block."""
+    w = synth.random_case(600 + block, B=1, Hq=2, Hkv=1, N=block * nblocks - 37, d=d, block=block, density=0.97,
+                          log_weights=True)
+    _log("case long rows block=%d d=%d N=%d" % (block, d, w.N))
+    _, res = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0)
+    rp = res.row_ptr.cpu().numpy()
+    assert np.diff(rp).max() > 1024
+    rows = sample_rows(w, seed=3, per_block=False)
+    stats = compare_rows(w, res, rows)
+    _log("  %s" % stats)
+    assert_within(stats)
