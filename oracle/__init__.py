@@ -45,7 +45,9 @@ def lib():
         L.oracle_perm_from_labels.restype = ctypes.c_int
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
-        L.oracle_schedule.argtypes = [P, I64, I64, I64, I64, I64, I64, P]
+        L.oracle_schedule.argtypes = [P, I64, I64, I64, I64, I64, I64, P, P]
+        L.oracle_spectral_order.restype = ctypes.c_int
+        L.oracle_spectral_order.argtypes = [P, P, I64, I64, I64, I64, P, P]
         L.oracle_attn_rows.restype = ctypes.c_int
         L.oracle_attn_rows.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
                                        P, P, P, P, P, ctypes.c_int, ctypes.c_double,
@@ -91,13 +93,32 @@ def perm_from_labels(labels: np.ndarray, n_clusters: int) -> np.ndarray:
     return perm
 
 
-def schedule(row_ptr: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int, n_xcd: int = 1):
+def schedule(row_ptr: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int, n_xcd: int = 1,
+             row_perm: Optional[np.ndarray] = None):
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    if row_perm is not None:
+        row_perm = np.ascontiguousarray(row_perm, dtype=np.int32).reshape(-1)
+        assert row_perm.size == B * Hq * nQB
     order = np.empty(B * Hq * nQB, dtype=np.int32)
-    rc = lib().oracle_schedule(_p(row_ptr), B, Hq, Hkv, nQB, W, n_xcd, _p(order))
+    rc = lib().oracle_schedule(_p(row_ptr), B, Hq, Hkv, nQB, W, n_xcd, _p(row_perm), _p(order))
     if rc:
         raise ValueError("oracle_schedule failed: %d" % rc)
     return order
+
+
+def spectral_order(row_ptr: np.ndarray, col: np.ndarray, BH: int, nQB: int, nKB: int, iters: int):
+    """WaveAlign stage-1 order of every head's query blocks.  Returns
+    (perm int32 [BH][nQB]: query block at each position, angle float64
+    [BH][nQB]: polar angle of each query block)."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    assert row_ptr.size == BH * nQB + 1
+    perm = np.empty(BH * nQB, dtype=np.int32)
+    angle = np.empty(BH * nQB, dtype=np.float64)
+    rc = lib().oracle_spectral_order(_p(row_ptr), _p(col), BH, nQB, nKB, iters, _p(perm), _p(angle))
+    if rc:
+        raise ValueError("oracle_spectral_order failed: %d" % rc)
+    return perm.reshape(BH, nQB), angle.reshape(BH, nQB)
 
 
 def attn_rows(q, k, v, row_ptr, col, lw, block: int, rows: np.ndarray, perm_q=None, perm_k=None,

@@ -26,6 +26,12 @@
  *                     descending nonzero-block count (WaveAlign, section IV-D,
  *                     NNZ-guided intra-wave alignment), then the launch-index
  *                     remap that gives each XCD a contiguous run.
+ *                     An optional per-head row order (below) replaces the
+ *                     query-block order inside each segment.
+ *  oracle_spectral_order
+ *                     WaveAlign stage 1 (section IV-C): rank-2 embedding of
+ *                     each head's mask rows by matrix-free centred subspace
+ *                     iteration (IV-C.2), rows ordered by polar angle (IV-C.1).
  *  oracle_attn_rows   Dense-masked softmax attention, InstaGen section 3.1
  *                     Eq. (1)-(3), with the per-block log-weight added to the
  *                     scaled logit (InstaGen Algorithm 1, Horvitz-Thompson
@@ -135,13 +141,15 @@ int oracle_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_
 /* row schedule                                                              */
 /* ------------------------------------------------------------------------ */
 /* Logical sequence: for each batch b and KV head g, the rows of the G = Hq/Hkv
- * query heads that share g, query block u outer and head inner.  Buckets of
+ * query heads that share g, position u outer and head inner; position u is
+ * query block u, or query block row_perm[head][u] when a per-head order is
+ * given.  Buckets of
  * at most W consecutive entries within one (b, g) segment are sorted by
  * (nnz descending, sequence position ascending).  With n_xcd > 1 the list is
  * then dealt so that launch index i runs logical position start(i % n_xcd) +
  * i / n_xcd, where XCD x receives the x-th contiguous slice. */
 int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t nQB,
-                    int64_t W, int64_t n_xcd, int32_t *order) {
+                    int64_t W, int64_t n_xcd, const int32_t *row_perm, int32_t *order) {
   if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W <= 0)
     return OR_ERR_ARG;
   int64_t G = Hq / Hkv, R = B * Hq * nQB, seg = G * nQB;
@@ -152,7 +160,11 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
   for (int64_t b = 0; b < B; ++b)
     for (int64_t g = 0; g < Hkv; ++g)
       for (int64_t u = 0; u < nQB; ++u)
-        for (int64_t j = 0; j < G; ++j) logical[pos++] = (int32_t)((b * Hq + g * G + j) * nQB + u);
+        for (int64_t j = 0; j < G; ++j) {
+          int64_t h = b * Hq + g * G + j;
+          int64_t uu = row_perm ? row_perm[h * nQB + u] : u;
+          logical[pos++] = (int32_t)(h * nQB + uu);
+        }
   for (int64_t s0 = 0; s0 < R; s0 += seg) {
     for (int64_t b0 = s0; b0 < s0 + seg; b0 += W) {
       int64_t n = (b0 + W <= s0 + seg) ? W : s0 + seg - b0;
@@ -181,6 +193,119 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
   free(buf);
   free(logical);
   return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* WaveAlign stage 1: polar spectral row order                               */
+/* ------------------------------------------------------------------------ */
+/* For every head bh (rows r = bh*nQB + u, u = 0..nQB-1) its mask M is the
+ * nQB x nKB 0/1 matrix of the listed blocks (entries outside [0, nKB) are
+ * ignored).  The centred mask C = M - 1 mu^T, mu[v] = (1/nQB) sum_u M[u][v],
+ * keeps pairwise row distances and sends the constant (workload) direction
+ * to a zero singular value (WaveAlign, section IV-C.2).  Its top-2 left
+ * singular subspace is found by subspace iteration X <- orth(C C^T X),
+ * applied without forming C: C^T X = M^T X - mu (1^T X) and
+ * C Z = M Z - 1 (mu^T Z).  The start is
+ *   X0[i] = ( ((37 i + 11) mod 101) / 101 - 1/2, ((53 i + 29) mod 97) / 97 - 1/2 )
+ * and orth is Gram-Schmidt on the two columns (a zero column stays zero).
+ * Row i is then placed by the polar angle atan2(X[i][1], X[i][0]) of its
+ * coordinates (section IV-C.1), ties by i.
+ * Out: perm[bh*nQB + p] = query block at position p; angle[bh*nQB + i] (or
+ * NULL). */
+static int cmp_angle_idx(const void *a, const void *b) {
+  const double *x = (const double *)a, *y = (const double *)b;
+  if (x[0] < y[0]) return -1;
+  if (x[0] > y[0]) return 1;
+  return (x[1] > y[1]) - (x[1] < y[1]);
+}
+
+static void orth2(double *x1, double *x2, int64_t n) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += x1[i] * x1[i];
+  double nrm = sqrt(s);
+  for (int64_t i = 0; i < n; ++i) x1[i] = nrm > 0.0 ? x1[i] / nrm : 0.0;
+  double d = 0.0;
+  for (int64_t i = 0; i < n; ++i) d += x1[i] * x2[i];
+  for (int64_t i = 0; i < n; ++i) x2[i] -= d * x1[i];
+  s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += x2[i] * x2[i];
+  nrm = sqrt(s);
+  for (int64_t i = 0; i < n; ++i) x2[i] = nrm > 0.0 ? x2[i] / nrm : 0.0;
+}
+
+int oracle_spectral_order(const int32_t *row_ptr, const int32_t *col, int64_t BH, int64_t nQB, int64_t nKB,
+                          int64_t iters, int32_t *perm, double *angle) {
+  if (!row_ptr || !col || !perm || BH <= 0 || nQB <= 0 || nKB <= 0 || iters < 1) return OR_ERR_ARG;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    double *x1 = malloc(sizeof(double) * nQB), *x2 = malloc(sizeof(double) * nQB);
+    double *y1 = malloc(sizeof(double) * nQB), *y2 = malloc(sizeof(double) * nQB);
+    double *z1 = malloc(sizeof(double) * nKB), *z2 = malloc(sizeof(double) * nKB);
+    double *mu = calloc((size_t)nKB, sizeof(double));
+    double *key = malloc(sizeof(double) * 2 * nQB);
+    if (!x1 || !x2 || !y1 || !y2 || !z1 || !z2 || !mu || !key) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+      const int32_t *rp = row_ptr + bh * nQB;
+      for (int64_t u = 0; u < nQB; ++u)
+        for (int32_t e = rp[u]; e < rp[u + 1]; ++e)
+          if (col[e] >= 0 && col[e] < nKB) mu[col[e]] += 1.0;
+      for (int64_t v = 0; v < nKB; ++v) mu[v] /= (double)nQB;
+      for (int64_t i = 0; i < nQB; ++i) {
+        x1[i] = (double)((37 * i + 11) % 101) / 101.0 - 0.5;
+        x2[i] = (double)((53 * i + 29) % 97) / 97.0 - 0.5;
+      }
+      for (int64_t it = 0; it < iters; ++it) {
+        /* Z = C^T X */
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t i = 0; i < nQB; ++i) {
+          s1 += x1[i];
+          s2 += x2[i];
+        }
+        for (int64_t v = 0; v < nKB; ++v) z1[v] = z2[v] = 0.0;
+        for (int64_t u = 0; u < nQB; ++u)
+          for (int32_t e = rp[u]; e < rp[u + 1]; ++e)
+            if (col[e] >= 0 && col[e] < nKB) {
+              z1[col[e]] += x1[u];
+              z2[col[e]] += x2[u];
+            }
+        for (int64_t v = 0; v < nKB; ++v) {
+          z1[v] -= mu[v] * s1;
+          z2[v] -= mu[v] * s2;
+        }
+        /* Y = C Z */
+        double t1 = 0.0, t2 = 0.0;
+        for (int64_t v = 0; v < nKB; ++v) {
+          t1 += mu[v] * z1[v];
+          t2 += mu[v] * z2[v];
+        }
+        for (int64_t u = 0; u < nQB; ++u) {
+          double a1 = 0.0, a2 = 0.0;
+          for (int32_t e = rp[u]; e < rp[u + 1]; ++e)
+            if (col[e] >= 0 && col[e] < nKB) {
+              a1 += z1[col[e]];
+              a2 += z2[col[e]];
+            }
+          y1[u] = a1 - t1;
+          y2[u] = a2 - t2;
+        }
+        orth2(y1, y2, nQB);
+        memcpy(x1, y1, sizeof(double) * nQB);
+        memcpy(x2, y2, sizeof(double) * nQB);
+      }
+      for (int64_t i = 0; i < nQB; ++i) {
+        key[2 * i] = atan2(x2[i], x1[i]);
+        key[2 * i + 1] = (double)i;
+        if (angle) angle[bh * nQB + i] = key[2 * i];
+      }
+      qsort(key, (size_t)nQB, 2 * sizeof(double), cmp_angle_idx);
+      for (int64_t p = 0; p < nQB; ++p) perm[bh * nQB + p] = (int32_t)key[2 * p + 1];
+    }
+    free(x1); free(x2); free(y1); free(y2); free(z1); free(z2); free(mu); free(key);
+  }
+  return bad ? OR_ERR_ARG : OR_OK;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -129,13 +129,14 @@ def test_perm_matches_stable_argsort():
     assert np.all(np.sort(perm, 1) == np.arange(1000)[None])
 
 
-def sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd):
+def sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm=None):
     G = Hq // Hkv
     nnz = np.diff(row_ptr)
     logical = []
+    blk = (lambda h, u: u) if row_perm is None else (lambda h, u: int(row_perm[h][u]))
     for b in range(B):
         for g in range(Hkv):
-            seg = [(b * Hq + g * G + j) * nQB + u for u in range(nQB) for j in range(G)]
+            seg = [(b * Hq + g * G + j) * nQB + blk(b * Hq + g * G + j, u) for u in range(nQB) for j in range(G)]
             for s in range(0, len(seg), W):
                 bucket = seg[s:s + W]
                 logical += [r for _, _, r in sorted((-int(nnz[r]), i, r) for i, r in enumerate(bucket))]
@@ -156,6 +157,22 @@ def test_schedule_matches_brute_force(B, Hq, Hkv, nQB, W, n_xcd):
     order = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd)
     np.testing.assert_array_equal(order, sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd))
     assert np.array_equal(np.sort(order), np.arange(B * Hq * nQB))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nQB,W,n_xcd", [(1, 4, 4, 37, 8, 1), (2, 8, 2, 20, 16, 8), (1, 3, 1, 50, 1, 1)])
+def test_schedule_with_row_order_matches_brute_force(B, Hq, Hkv, nQB, W, n_xcd):
+    rng = np.random.default_rng(B * 300 + Hq + nQB)
+    sizes = rng.integers(0, 9, size=B * Hq * nQB)
+    row_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    row_perm = np.stack([rng.permutation(nQB) for _ in range(B * Hq)]).astype(np.int32)
+    order = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm)
+    np.testing.assert_array_equal(order, sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm))
+    # identity order = no order; W = 1 keeps the given order untouched
+    ident = np.tile(np.arange(nQB, dtype=np.int32), (B * Hq, 1))
+    np.testing.assert_array_equal(oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, ident),
+                                  oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd))
+    if W == 1 and n_xcd == 1 and Hq == Hkv:
+        np.testing.assert_array_equal(order, (np.arange(B * Hq)[:, None] * nQB + row_perm).reshape(-1))
 
 
 def test_schedule_buckets_longest_first():
