@@ -21,7 +21,8 @@ BSA_V_DIM_MAJOR = 1
 
 # Every symbol include/bsattn.h declares.
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_perm_from_labels",
-           "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_schedule", "bsa_attn_fwd",
+           "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
+           "bsa_attn_fwd",
            "bsa_device_cus", "bsa_device_clock_khz")
 
 
@@ -76,7 +77,9 @@ def load():
         L.bsa_transpose_rows.restype = ctypes.c_int
         L.bsa_transpose_rows.argtypes = [P, P, P, I32, I32, I64, I32, I64, P, P, P]
         L.bsa_schedule.restype = ctypes.c_int
-        L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P]
+        L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, P]
+        L.bsa_spectral_order.restype = ctypes.c_int
+        L.bsa_spectral_order.argtypes = [P, P, I32, I32, I32, I32, P, P, P]
         L.bsa_attn_fwd.restype = ctypes.c_int
         L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
         L.bsa_device_cus.restype = ctypes.c_int

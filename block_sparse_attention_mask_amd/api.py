@@ -162,13 +162,32 @@ def transpose_rows(src: torch.Tensor, perm: Optional[torch.Tensor] = None, ld: O
 
 
 def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_rows: int = 0,
-             n_xcd: int = 8, order=None, stream=None) -> torch.Tensor:
+             n_xcd: int = 8, order=None, stream=None, row_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
     _dev(row_ptr, "row_ptr", torch.int32)
+    if row_perm is not None:
+        _dev(row_perm, "row_perm", torch.int32)
+        if row_perm.numel() != B * Hq * nQB:
+            raise ValueError("row_perm must hold B*Hq*nQB entries")
     if order is None:
         order = torch.empty(B * Hq * nQB, dtype=torch.int32, device=row_ptr.device)
     check("bsa_schedule", load().bsa_schedule(_ptr(row_ptr), B, Hq, Hkv, nQB, int(wave_rows), int(n_xcd),
-                                              _ptr(order), _stream(stream)))
+                                              _ptr(row_perm), _ptr(order), _stream(stream)))
     return order
+
+
+def spectral_order(row_ptr: torch.Tensor, col: torch.Tensor, BH: int, nQB: int, nKB: int, iters: int = 10,
+                   want_angle: bool = False, stream=None):
+    """WaveAlign stage-1 order of every head's query blocks: (perm int32
+    [BH][nQB], angle float64 [BH][nQB] or None)."""
+    _dev(row_ptr, "row_ptr", torch.int32)
+    _dev(col, "col", torch.int32)
+    if row_ptr.numel() != BH * nQB + 1:
+        raise ValueError("row_ptr must hold BH*nQB + 1 entries")
+    perm = torch.empty((BH, nQB), dtype=torch.int32, device=row_ptr.device)
+    angle = torch.empty((BH, nQB), dtype=torch.float64, device=row_ptr.device) if want_angle else None
+    check("bsa_spectral_order", load().bsa_spectral_order(_ptr(row_ptr), _ptr(col), BH, nQB, nKB, int(iters),
+                                                          _ptr(perm), _ptr(angle), _stream(stream)))
+    return perm, angle
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,

@@ -14,6 +14,9 @@
 // x receives the x-th contiguous slice, keeping neighbouring rows (which
 // share K/V blocks) in one L2.
 //
+// A stage-1 order (WaveAlign section IV-C, bsa_spectral_order) may replace
+// the query-block order within each head before the buckets are formed.
+//
 // One workgroup per bucket: keys (INT32_MAX - nnz) << 32 | position are
 // sorted ascending with a bitonic network in LDS.
 #include "bsa_internal.h"
@@ -24,7 +27,8 @@ constexpr int kMaxWave = 2048;
 
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ row_ptr, int Hq,
                                                         int Hkv, int nQB, int W, int n_xcd,
-                                                        int64_t R, int32_t *__restrict__ order) {
+                                                        int64_t R, const int32_t *__restrict__ row_perm,
+                                                        int32_t *__restrict__ order) {
   __shared__ uint64_t key[kMaxWave];
   const int G = Hq / Hkv;
   const int64_t seg = (int64_t)G * nQB;
@@ -35,13 +39,18 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   int P2 = 1;
   while (P2 < n) P2 <<= 1;
   const int64_t b = s / Hkv, g = s % Hkv;
+  // row at segment position j: head (b, g G + j % G), query block j / G (or
+  // its stage-1 replacement); -1 for a corrupt stage-1 entry
+  auto row_at = [&](int64_t j) -> int64_t {
+    const int64_t p = j / G, h = b * Hq + g * G + j % G;
+    const int64_t u = row_perm ? (int64_t)row_perm[h * nQB + p] : p;
+    return (u >= 0 && u < nQB) ? h * nQB + u : -1;
+  };
   for (int i = threadIdx.x; i < P2; i += 1024) {
     uint64_t kk = ~0ull;
     if (i < n) {
-      const int64_t j = k * W + i;                  // position within the segment
-      const int64_t u = j / G, hh = j % G;
-      const int64_t r = (b * Hq + g * G + hh) * nQB + u;
-      const int32_t nnz = row_ptr[r + 1] - row_ptr[r];
+      const int64_t r = row_at(k * W + i);          // position within the segment
+      const int32_t nnz = r >= 0 ? row_ptr[r + 1] - row_ptr[r] : 0;
       kk = ((uint64_t)(uint32_t)(0x7fffffff - nnz) << 32) | (uint32_t)i;
     }
     key[i] = kk;
@@ -64,9 +73,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   }
   for (int i = threadIdx.x; i < n; i += 1024) {
     const int src = (int)(key[i] & 0xffffffffu);
-    const int64_t j = k * W + src;
-    const int64_t u = j / G, hh = j % G;
-    const int32_t r = (int32_t)((b * Hq + g * G + hh) * nQB + u);
+    const int32_t r = (int32_t)row_at(k * W + src);
     const int64_t P = start + i;                    // logical position
     int64_t launch = P;
     if (n_xcd > 1) {
@@ -87,7 +94,8 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
 }  // namespace
 
 extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
-                            int32_t wave_rows, int32_t n_xcd, int32_t *order, bsa_stream_t stream) {
+                            int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm, int32_t *order,
+                            bsa_stream_t stream) {
   if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
   if (Hq % Hkv) return BSA_ERR_ARG;
   if (wave_rows < 0 || n_xcd < 0 || n_xcd > 64) return BSA_ERR_ARG;
@@ -101,7 +109,7 @@ extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32
   const int64_t seg = (int64_t)(Hq / Hkv) * nQB;
   const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),
-                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, order);
+                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, row_perm, order);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

@@ -72,9 +72,11 @@ class StepResult:
 
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
-            v_dim_major: bool = True, stream=None) -> StepResult:
+            v_dim_major: bool = True, stream=None, stage1_iters: int = 0) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
-    recorded around the attention launch on the same stream."""
+    recorded around the attention launch on the same stream.  With
+    ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
+    each head's query blocks (that many subspace iterations)."""
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag,
                                      stream=stream)
     q, k, v = dw.q, dw.k, dw.v
@@ -90,7 +92,12 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
         v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=stream)
     order = None
     if schedule:
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream)
+        row_perm = None
+        if stage1_iters > 0:
+            row_perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, stage1_iters,
+                                             stream=stream)
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
+                             row_perm=row_perm)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:

@@ -142,6 +142,28 @@ int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t 
                        const int64_t dst_strides[3], bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * WaveAlign stage 1: polar spectral order of each head's query blocks.
+ *
+ * Source: WaveAlign, section IV-C (C.1 polar spectral ordering of a rank-2
+ * embedding of the mask rows; C.2 matrix-free centred subspace iteration).
+ *
+ * For every head h in [0, BH) (CSR rows h*nQB .. h*nQB + nQB - 1): the
+ * nQB x nKB 0/1 block mask M is centred, C = M - 1 mu^T with mu the column
+ * means; `iters` steps of X <- orth(C C^T X) (Gram-Schmidt, start
+ * X0[u] = (((37u + 11) mod 101)/101 - 1/2, ((53u + 29) mod 97)/97 - 1/2))
+ * give rank-2 row coordinates, and rows are ordered by their polar angle
+ * atan2(X[u][1], X[u][0]), ties by u.  fp64 throughout.
+ * row_ptr: device int32 [BH*nQB + 1]; col: device int32 [nnz] (entries
+ * outside [0, nKB) are ignored).  perm: device int32 [BH][nQB] (output):
+ * perm[h][p] = query block at position p, a permutation of 0..nQB-1 per head.
+ * angle: device float64 [BH][nQB] (output, may be NULL): the angle of each
+ * query block.  nQB, nKB <= 1024 and nKB * ceil(nQB / 32) <= 24576, else
+ * BSA_ERR_UNSUPPORTED; iters >= 1.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, int32_t nQB, int32_t nKB,
+                       int32_t iters, int32_t *perm, double *angle, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Row schedule (launch order of the attention kernel).
  *
  * Source: WaveAlign, section IV-D (rows in consecutive buckets of at most W,
@@ -149,18 +171,22 @@ int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t 
  * section VI-B (sequential-head scheduling).
  *
  * Logical sequence: for each batch b and KV head g, the rows of the
- * G = Hq / Hkv query heads sharing g, query block u outer and head inner
- * (identity stage-1 order).  Buckets of `wave_rows` consecutive entries within
- * each (b, g) segment are sorted by (nnz descending, sequence position
- * ascending).  When n_xcd > 1 the list is dealt to launch indices so that the
- * GPU's round-robin dispatch gives XCD x the x-th contiguous slice:
+ * G = Hq / Hkv query heads sharing g, position p outer and head inner; the
+ * row at position p of head h is query block p, or query block
+ * row_perm[h][p] when a stage-1 order is given (row_perm: device int32
+ * [B*Hq][nQB], a permutation of 0..nQB-1 per head, or NULL; an entry outside
+ * [0, nQB) yields launch entry -1, which the attention kernel skips).
+ * Buckets of `wave_rows` consecutive entries within each (b, g) segment are
+ * sorted by (nnz descending, sequence position ascending).  When n_xcd > 1
+ * the list is dealt to launch indices so that the GPU's round-robin dispatch
+ * gives XCD x the x-th contiguous slice:
  * order[i] = logical[start(i % n_xcd) + i / n_xcd].  wave_rows = 0 selects
  * 2048 (a whole segment of up to 2048 rows is one bucket).  row_ptr: device
  * int32 [R+1]; order: device int32 [R] (output).  wave_rows <= 2048.
  * Asynchronous.
  * ------------------------------------------------------------------------- */
-int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
-                 int32_t wave_rows, int32_t n_xcd, int32_t *order, bsa_stream_t stream);
+int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB, int32_t wave_rows,
+                 int32_t n_xcd, const int32_t *row_perm, int32_t *order, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Block-sparse attention forward.

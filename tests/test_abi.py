@@ -83,10 +83,19 @@ def test_perm_argument_errors(L):
 
 
 def test_schedule_argument_errors(L):
-    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
+
+
+def test_spectral_order_argument_errors(L):
+    assert L.bsa_spectral_order(None, FAKE, 4, 100, 100, 10, FAKE, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 0, FAKE, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 10, None, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 0, 100, 100, 10, FAKE, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1025, 100, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1024, 1024, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def _args(**kw):

@@ -45,6 +45,14 @@ def test_config_parity(name):
     W = 2048   # wave_rows = 0 selects one bucket per segment of up to 2048 rows
     assert np.array_equal(res.order.cpu().numpy(), oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8))
     _log("  integer steps bit-exact (nnz=%d)" % rp[-1])
+    # stage-1 order of every head and the schedule built on it
+    gp, ga = api.spectral_order(res.row_ptr, res.col, w.B * w.Hq, w.nQB, w.nQB, 10, want_angle=True)
+    operm, oang = oracle.spectral_order(rp, col, w.B * w.Hq, w.nQB, w.nQB, 10)
+    from test_gpu_parity import _check_spectral
+    _check_spectral(gp.cpu().numpy(), ga.cpu().numpy(), operm, oang)
+    so = api.schedule(res.row_ptr, w.B, w.Hq, w.Hkv, w.nQB, 256, 8, row_perm=gp).cpu().numpy()
+    assert np.array_equal(so, oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, 256, 8, gp.cpu().numpy()))
+    _log("  stage-1 order and schedule match")
     if name == "tiny":
         rows = np.arange(w.B * w.Hq * w.N, dtype=np.int64)
     else:

@@ -163,3 +163,57 @@ def test_long_rows_span_list_chunks(block, d, nblocks):
     stats = compare_rows(w, res, rows)
     _log("  %s" % stats)
     assert_within(stats)
+
+
+def _check_spectral(gperm, gang, operm, oang):
+    """Orders equal except among rows whose angles tie within 1e-9 (fp64 sums
+    in different orders on the two sides); angles equal within 1e-9."""
+    d = np.abs(((gang - oang) + np.pi) % (2 * np.pi) - np.pi)
+    assert d.max() < 1e-9, d.max()
+    for h in range(gperm.shape[0]):
+        if np.array_equal(gperm[h], operm[h]):
+            continue
+        bad = np.nonzero(gperm[h] != operm[h])[0]
+        a = oang[h][operm[h][bad]]
+        b = oang[h][gperm[h][bad]]
+        assert np.abs(a - b).max() < 1e-9, (h, bad[:8])
+        assert sorted(gperm[h].tolist()) == list(range(gperm.shape[1]))
+
+
+@pytest.mark.parametrize("BH,nQB,density,iters", [(3, 100, 0.2, 10), (2, 591, 0.15, 10), (4, 37, 0.5, 15),
+                                                  (1, 768, 0.05, 6)])
+def test_spectral_order_matches_oracle(BH, nQB, density, iters):
+    rng = np.random.default_rng(BH * 1000 + nQB)
+    protos = rng.random((5, nQB)) < density
+    lab = rng.integers(0, 5, size=BH * nQB)
+    m = (protos[lab] ^ (rng.random((BH * nQB, nQB)) < 0.03)).astype(np.uint8)
+    rows, cols = np.nonzero(m)
+    rp = np.concatenate([[0], np.cumsum(m.sum(1))]).astype(np.int32)
+    col = cols.astype(np.int32)
+    _log("case spectral BH=%d nQB=%d" % (BH, nQB))
+    gp, ga = api.spectral_order(torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda(), BH, nQB, nQB, iters,
+                                want_angle=True)
+    operm, oang = oracle.spectral_order(rp, col, BH, nQB, nQB, iters)
+    _check_spectral(gp.cpu().numpy(), ga.cpu().numpy(), operm, oang)
+
+
+def test_schedule_with_row_order_bit_exact():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, nQB, W, n_xcd = 2, 8, 2, 40, 16, 8
+    sizes = rng.integers(0, 30, size=B * Hq * nQB)
+    row_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    row_perm = np.stack([rng.permutation(nQB) for _ in range(B * Hq)]).astype(np.int32)
+    _log("case schedule with row order")
+    got = api.schedule(torch.from_numpy(row_ptr).cuda(), B, Hq, Hkv, nQB, W, n_xcd,
+                       row_perm=torch.from_numpy(row_perm).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm))
+
+
+def test_stage1_schedule_leaves_outputs_unchanged():
+    w = make("b128_d128_perm_lw")
+    _log("case stage-1 schedule invariance")
+    _, r1 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16)
+    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16, stage1_iters=8)
+    assert not np.array_equal(r1.order.cpu().numpy(), r2.order.cpu().numpy())
+    assert np.array_equal(r1.out.cpu().numpy(), r2.out.cpu().numpy())
+    assert np.array_equal(r1.lse.cpu().numpy(), r2.lse.cpu().numpy())
