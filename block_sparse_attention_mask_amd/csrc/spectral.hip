@@ -12,20 +12,21 @@
 // 101 - 1/2, ((53 u + 29) mod 97) / 97 - 1/2) and Gram-Schmidt for orth
 // (a zero column stays zero).
 //
-// One workgroup per head; everything but the CSR list lives in LDS.  M^T X
-// is summed per column over a column-major bitmask of the mask (rows in
-// ascending order), M Z per row over its CSR list, and every sum over rows
-// or columns is a fixed strided-then-tree reduction, so the result does not
-// depend on timing.  Arithmetic is fp64 (the work is O(nnz) per iteration).
+// One workgroup per head, working in LDS.  The mask is held twice as a
+// bitmask: column-major for M^T X (each column sums its rows in ascending
+// order) and row-major for M Z (each row sums its blocks in ascending
+// order); every sum over rows or columns is a fixed strided-then-tree
+// reduction, so the result does not depend on timing.  Arithmetic is fp64
+// (the work is O(nnz) per iteration).
 #include <math.h>
 
 #include "bsa_internal.h"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kMaxRows = 1024;             // nQB and nKB per head
-constexpr int kMaxWords = 24576;           // bitmask words: nKB * ceil(nQB / 32)
+constexpr int kMaxWords = 12288;           // words of each bitmask: nKB * ceil(nQB / 32), nQB * ceil(nKB / 32)
 
 struct alignas(16) Sums {
   double a, b;
@@ -54,19 +55,24 @@ __global__ __launch_bounds__(kThreads) void spectral_order_kernel(const int32_t 
                                                                   int nKB, int iters, int32_t *__restrict__ perm,
                                                                   double *__restrict__ angle) {
   __shared__ uint32_t bits[kMaxWords];     // bits[v * nw + u / 32] bit u % 32: block v listed in row u
+  __shared__ uint32_t rbits[kMaxWords];    // rbits[u * nwk + v / 32] bit v % 32: the same, row-major
   __shared__ double x1[kMaxRows], x2[kMaxRows], z1[kMaxRows], z2[kMaxRows], mu[kMaxRows];
   __shared__ double red[2 * kThreads];
   const int t = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int32_t *rp = row_ptr + bh * nQB;
-  const int nw = (nQB + 31) / 32;
+  const int nw = (nQB + 31) / 32, nwk = (nKB + 31) / 32;
 
   for (int i = t; i < nKB * nw; i += kThreads) bits[i] = 0u;
+  for (int i = t; i < nQB * nwk; i += kThreads) rbits[i] = 0u;
   __syncthreads();
   for (int u = t; u < nQB; u += kThreads)
     for (int32_t e = rp[u]; e < rp[u + 1]; ++e) {
       const int32_t v = col[e];
-      if (v >= 0 && v < nKB) atomicOr(&bits[v * nw + u / 32], 1u << (u % 32));
+      if (v >= 0 && v < nKB) {
+        atomicOr(&bits[v * nw + u / 32], 1u << (u % 32));
+        atomicOr(&rbits[u * nwk + v / 32], 1u << (v % 32));
+      }
     }
   __syncthreads();
   for (int v = t; v < nKB; v += kThreads) {
@@ -112,9 +118,11 @@ __global__ __launch_bounds__(kThreads) void spectral_order_kernel(const int32_t 
     const Sums tt = block_sum2(p1, p2, red);
     for (int u = t; u < nQB; u += kThreads) {
       double a1 = 0.0, a2 = 0.0;
-      for (int32_t e = rp[u]; e < rp[u + 1]; ++e) {
-        const int32_t v = col[e];
-        if (v >= 0 && v < nKB) {
+      for (int w = 0; w < nwk; ++w) {
+        uint32_t m = rbits[u * nwk + w];
+        while (m) {
+          const int v = 32 * w + __builtin_ctz(m);
+          m &= m - 1;
           a1 += z1[v];
           a2 += z2[v];
         }
@@ -167,7 +175,8 @@ extern "C" int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, in
                                   int32_t nKB, int32_t iters, int32_t *perm, double *angle,
                                   bsa_stream_t stream) {
   if (!row_ptr || !col || !perm || BH <= 0 || nQB <= 0 || nKB <= 0 || iters < 1) return BSA_ERR_ARG;
-  if (nQB > kMaxRows || nKB > kMaxRows || (int64_t)nKB * ((nQB + 31) / 32) > kMaxWords)
+  if (nQB > kMaxRows || nKB > kMaxRows || (int64_t)nKB * ((nQB + 31) / 32) > kMaxWords ||
+      (int64_t)nQB * ((nKB + 31) / 32) > kMaxWords)
     return BSA_ERR_UNSUPPORTED;
   if ((int64_t)BH * nQB >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(spectral_order_kernel, dim3((unsigned)BH), dim3(kThreads), 0, bsa_hip_stream(stream), row_ptr,

@@ -157,7 +157,8 @@ int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t 
  * outside [0, nKB) are ignored).  perm: device int32 [BH][nQB] (output):
  * perm[h][p] = query block at position p, a permutation of 0..nQB-1 per head.
  * angle: device float64 [BH][nQB] (output, may be NULL): the angle of each
- * query block.  nQB, nKB <= 1024 and nKB * ceil(nQB / 32) <= 24576, else
+ * query block.  nQB, nKB <= 1024, nKB * ceil(nQB / 32) <= 12288 and
+ * nQB * ceil(nKB / 32) <= 12288 (e.g. 614 x 614 or 512 x 768), else
  * BSA_ERR_UNSUPPORTED; iters >= 1.  Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, int32_t nQB, int32_t nKB,

@@ -96,6 +96,7 @@ def test_spectral_order_argument_errors(L):
     assert L.bsa_spectral_order(FAKE, FAKE, 0, 100, 100, 10, FAKE, None, None) == _lib.BSA_ERR_ARG
     assert L.bsa_spectral_order(FAKE, FAKE, 4, 1025, 100, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
     assert L.bsa_spectral_order(FAKE, FAKE, 4, 1024, 1024, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 700, 700, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def _args(**kw):

@@ -181,7 +181,7 @@ def _check_spectral(gperm, gang, operm, oang):
 
 
 @pytest.mark.parametrize("BH,nQB,density,iters", [(3, 100, 0.2, 10), (2, 591, 0.15, 10), (4, 37, 0.5, 15),
-                                                  (1, 768, 0.05, 6)])
+                                                  (1, 600, 0.05, 6)])
 def test_spectral_order_matches_oracle(BH, nQB, density, iters):
     rng = np.random.default_rng(BH * 1000 + nQB)
     protos = rng.random((5, nQB)) < density
