@@ -39,8 +39,11 @@
 //     row-to-key map of key_of_row, so the eight probabilities a lane holds
 //     per PV k-step are eight consecutive keys and the V^T operand is one
 //     16-byte read.
-//   * Softmax in base 2, fp32; the running max is raised (and O rescaled)
-//     only when a tile's max exceeds it by more than 8.
+//   * Softmax in base 2, fp32, p = 2^(c s + lw - m) with c = log2(e)/sqrt(d).
+//     No per-tile max is taken: the running max m (starting at 0) is raised,
+//     O and l rescaled and the tile's exponentials redone, only when a
+//     lane's 32 probabilities of the tile sum past 32 * 2^8 (so some
+//     probability exceeded 2^8) or nothing has been accumulated yet.
 //   * K tile offsets go into the range-checked lane offset, so rows at or
 //     past N of a partial last block read as zeros; V^T rows hold every key
 //     of every block, so their tile offset is scalar.
@@ -183,7 +186,7 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   // buffer a step touches is a known object.
   auto half = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = 0.f, l_run = 0.f;
     f32x16 o[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -284,24 +287,11 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           for (int e = 0; e < 16; ++e)
             if (32 * jj + 16 * (e >> 3) + (e & 7) >= lim) s[jj][e] = -INFINITY;
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jj = 0; jj < C::MTW; ++jj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jj][e]);
-      mx = halves_max(mx);
-      const float m_tile = (mx == -INFINITY) ? -INFINITY : fmaf(mx, p.c, bias);
-      if (__any(m_tile > m_run + kTau)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-        m_run = m_new;
-      }
-      const float nb = bias - (m_run == -INFINITY ? 0.f : m_run);
+      // exponentials against the running max; it is raised only when a lane's
+      // 32 probabilities sum past 32 * 2^8 (some probability above 2^8) or
+      // nothing has been accumulated yet, and then the tile is redone
+      float nb = bias - m_run;
+      float ls = 0.f;
 #pragma unroll
       for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
@@ -309,7 +299,7 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           float pv[8];
 #pragma unroll
           for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
-          l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+          ls += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
           pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
                                                              cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
           const int gi = 2 * jj + s2;   // exponential group; its copies follow it
@@ -318,6 +308,37 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           for (int t = gi * C::NSLOT / (2 * C::MTW); t < (gi + 1) * C::NSLOT / (2 * C::MTW); ++t)
             copy_slot(t, kd, vd, sr);
         }
+      if (__any(ls > 32.f * 256.f || l_run + ls == 0.f)) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < C::MTW; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = fmaxf(m, fmaf(s[jj][e], p.c, nb));
+        m = halves_max(m);
+        const float lsum = halves_sum(ls), lrun = halves_sum(l_run);
+        const float sh = (m > kTau || (lrun + lsum == 0.f && m > -INFINITY)) ? m : 0.f;
+        m_run += sh;
+        nb = bias - m_run;
+        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+        ls = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < C::MTW; ++jj)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float pv[8];
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
+            ls += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+            pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                                                               cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
+          }
+      }
+      l_run += ls;
     };
 
     // Phase loop.  Half 0 runs M(0) E(0) M(1) ... E(n-1) M(n) in phases
