@@ -42,6 +42,10 @@ def lib():
         L.oracle_build_csr.restype = I64
         L.oracle_build_csr.argtypes = [P, P, ctypes.c_float, P, I64, I64, I64, ctypes.c_int,
                                        P, P, P, I64]
+        L.oracle_build_crm.restype = ctypes.c_int
+        L.oracle_build_crm.argtypes = [P, P, ctypes.c_float, I64, I64, I64, ctypes.c_int, P]
+        L.oracle_crm_walk.restype = I64
+        L.oracle_crm_walk.argtypes = [P, I64, I64, P, P, I64]
         L.oracle_perm_from_labels.restype = ctypes.c_int
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
@@ -81,6 +85,36 @@ def build_csr(mask=None, T=None, p: float = 0.0, lw_map=None, nQB: int = 0, forc
                                 int(force_diag), _p(row_ptr), _p(col), _p(lw), n)
     assert n2 == n
     return row_ptr, col[:n], (None if lw is None else lw[:n])
+
+
+def build_crm(mask=None, T=None, p: float = 0.0, nQB: int = 0, force_diag: bool = True):
+    """Returns CRM words uint32 [R][ceil(nKB / 32)]."""
+    src = mask if mask is not None else T
+    R, nKB = src.shape
+    mask = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    T = None if T is None else np.ascontiguousarray(T, dtype=np.float32)
+    words = np.empty((R, (nKB + 31) // 32), dtype=np.uint32)
+    rc = lib().oracle_build_crm(_p(mask), _p(T), float(p), R, nQB or nKB, nKB, int(force_diag),
+                                _p(words))
+    if rc:
+        raise ValueError("oracle_build_crm failed: %d" % rc)
+    return words
+
+
+def crm_walk(words: np.ndarray, nKB: int):
+    """Runs the CRM forward iterator over every row of ``words`` [R][W].
+    Returns (row_ptr int32[R+1], col int32[nnz])."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    R, W = words.shape
+    assert W == (nKB + 31) // 32
+    row_ptr = np.zeros(R + 1, dtype=np.int32)
+    n = lib().oracle_crm_walk(_p(words), R, nKB, _p(row_ptr), None, 0)
+    if n < 0:
+        raise ValueError("oracle_crm_walk failed: %d" % n)
+    col = np.zeros(max(n, 1), dtype=np.int32)
+    n2 = lib().oracle_crm_walk(_p(words), R, nKB, _p(row_ptr), _p(col), n)
+    assert n2 == n
+    return row_ptr, col[:n]
 
 
 def perm_from_labels(labels: np.ndarray, n_clusters: int) -> np.ndarray:

@@ -16,6 +16,21 @@
  *                     forward iterator of ScalingAttention (section 7.3,
  *                     Algorithm 2) walks the active KV blocks.  Log-weights
  *                     are copied bit for bit from the log-weight map.
+ *  oracle_build_crm   Block mask -> CRM rows (ScalingAttention, section 7.2:
+ *                     Compressed Row Mask): each row is an array of
+ *                     ceil(nKB / 32) uint32 words, bit (v mod 32) of word
+ *                     (v / 32) set when KV block v is kept (same keep rule
+ *                     as oracle_build_csr); bits at v >= nKB stay clear.
+ *  oracle_crm_walk    The CRM forward iterator (ScalingAttention, section 7.3,
+ *                     Algorithm 2) run over every row: the state holds the
+ *                     next word, the last word, the current word's remaining
+ *                     bits and the index of its bit 0 (one word before the
+ *                     row at the start); loading a word moves that index on
+ *                     by 32, a cleared word loads the next one, each step
+ *                     yields base + count-trailing-zeros and clears the
+ *                     lowest bit.  Bits of the last word at v >= nKB are
+ *                     not part of the row and are skipped.  Writes the
+ *                     yielded indices as CSR.
  *  oracle_perm_from_labels
  *                     Gather permutation that makes every cluster contiguous
  *                     (InstaGen, section 4: tokens permuted into contiguous
@@ -96,6 +111,74 @@ int64_t oracle_build_csr(const uint8_t *mask, const float *T, float p, const flo
         }
       }
       ++n;
+    }
+    row_ptr[r + 1] = (int32_t)n;
+  }
+  return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* mask -> CRM, CRM -> CSR by the forward iterator                           */
+/* ------------------------------------------------------------------------ */
+/* words[r * W + v / 32] bit v % 32, W = ceil(nKB / 32). */
+int oracle_build_crm(const uint8_t *mask, const float *T, float p, int64_t R, int64_t nQB,
+                     int64_t nKB, int force_diag, uint32_t *words) {
+  if ((!mask && !T) || R < 0 || nQB <= 0 || nKB <= 0 || !words) return OR_ERR_ARG;
+  int64_t W = (nKB + 31) / 32;
+  for (int64_t r = 0; r < R; ++r) {
+    uint32_t *row = words + r * W;
+    for (int64_t w = 0; w < W; ++w) row[w] = 0u;
+    for (int64_t v = 0; v < nKB; ++v)
+      if (kept(mask, T, p, r, v, nQB, nKB, force_diag)) row[v / 32] |= (uint32_t)1 << (v % 32);
+  }
+  return OR_OK;
+}
+
+/* Iterator state over one row's words. */
+typedef struct {
+  const uint32_t *ptr, *end; /* next word to load, one past the last */
+  uint32_t val;              /* bits of the current word not yet yielded */
+  int64_t base;              /* KV-block index of bit 0 of the current word */
+  uint32_t tail;             /* bits of the last word that name blocks below nKB */
+} crm_iter;
+
+static int trailing_zeros(uint32_t x) { /* x != 0 */
+  int n = 0;
+  while (!(x & 1u)) {
+    x >>= 1;
+    ++n;
+  }
+  return n;
+}
+
+/* Loads words until one with a set bit is current or the row is used up. */
+static void crm_advance(crm_iter *s) {
+  while (s->val == 0u && s->ptr < s->end) {
+    s->val = *s->ptr++;
+    if (s->ptr == s->end) s->val &= s->tail;
+    s->base += 32;
+  }
+}
+
+/* Fills row_ptr[R+1]; when col != NULL also col.  Returns nnz, or a negative
+ * error. */
+int64_t oracle_crm_walk(const uint32_t *words, int64_t R, int64_t nKB, int32_t *row_ptr, int32_t *col,
+                        int64_t capacity) {
+  if (!words || R < 0 || nKB <= 0 || !row_ptr) return OR_ERR_ARG;
+  int64_t W = (nKB + 31) / 32, n = 0;
+  row_ptr[0] = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    crm_iter s = {words + r * W, words + (r + 1) * W, 0u, -32,
+                  nKB % 32 ? ((uint32_t)1 << (nKB % 32)) - 1u : ~0u};
+    crm_advance(&s);
+    while (s.val != 0u) {
+      if (col) {
+        if (n >= capacity) return OR_ERR_CAPACITY;
+        col[n] = (int32_t)(s.base + trailing_zeros(s.val));
+      }
+      ++n;
+      s.val &= s.val - 1u;
+      if (s.val == 0u) crm_advance(&s);
     }
     row_ptr[r + 1] = (int32_t)n;
   }
