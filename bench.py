@@ -109,6 +109,15 @@ def main():
     # the attention launch alone: 10 warm-up calls, median of 50; then one
     # launch after a 1 GiB write has evicted L2 and MALL
     attn_solo = attention_alone(dw, args, torch)
+    # the same launch with CRM rows in place of the CSR lists (workloads
+    # without log-weights), and the mask -> CRM stage
+    crm = None
+    if dw.lw_map is None:
+        crm_solo = attention_alone(dw, args, torch, crm=True)
+        W = -(-w.nQB // 32)
+        crm = {"alone_median50_ms": crm_solo["median_ms"], "l2_flushed_ms": crm_solo["flushed_ms"],
+               "mask_to_crm_ms": crm_stage_ms(dw, torch),
+               "list_bytes_per_row": {"crm": 4 * W, "csr": round(4.0 + 4.0 * nnz / w.R, 1)}}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
@@ -154,6 +163,7 @@ def main():
                         "l2_flushed_ms": attn_solo["flushed_ms"]},
         "device": device_info(torch),
         "stages_ms": stages,
+        "crm_lists": crm,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config),
@@ -182,11 +192,18 @@ def attn_sources_sha256():
     return h.hexdigest()
 
 
-def attention_alone(dw, args, torch):
+def attention_alone(dw, args, torch, crm=False):
     """The attention kernel by itself on its inputs (already permuted and
-    transposed), timed with HIP events on the current stream."""
+    transposed), timed with HIP events on the current stream.  With ``crm``
+    the lists are CRM rows."""
     from block_sparse_attention_mask_amd import api
-    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
+    crm_rows = None
+    if crm:
+        crm_rows = api.crm_build(dw.mask, dw.T, dw.p, dw.nQB, dw.force_diag)
+        row_ptr, _ = api.crm_row_ptr(crm_rows, dw.nQB, want_nnz=False)
+        col = lw = None
+    else:
+        row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
     q, k, pq, pk = dw.q, dw.k, None, None
     if dw.permuted:
         pq = api.perm_from_labels(dw.labels_q, dw.n_clusters)
@@ -199,7 +216,7 @@ def attention_alone(dw, args, torch):
 
     def launch():
         api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
-                     causal=dw.causal, v_dim_major=True, out=out)
+                     causal=dw.causal, v_dim_major=True, out=out, crm=crm_rows)
 
     for _ in range(10):
         launch()
@@ -220,6 +237,26 @@ def attention_alone(dw, args, torch):
     torch.cuda.synchronize()
     del flush
     return {"median_ms": round(float(np.median(ms)), 4), "flushed_ms": round(a.elapsed_time(b), 4)}
+
+
+def crm_stage_ms(dw, torch):
+    """Mask -> CRM rows and their row offsets (no host synchronisation):
+    median of 10 after 2 warm-up passes."""
+    from block_sparse_attention_mask_amd import api
+    s = torch.cuda.current_stream()
+    crm = api.crm_build(dw.mask, dw.T, dw.p, dw.nQB, dw.force_diag)
+    rp, _ = api.crm_row_ptr(crm, dw.nQB, want_nnz=False)
+    ms = []
+    for i in range(12):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        api.crm_build(dw.mask, dw.T, dw.p, dw.nQB, dw.force_diag, crm=crm)
+        api.crm_row_ptr(crm, dw.nQB, row_ptr=rp, want_nnz=False)
+        b.record(s)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(a.elapsed_time(b))
+    return round(float(np.median(ms)), 4)
 
 
 def device_info(torch):

@@ -20,7 +20,8 @@ BSA_V_TOKEN_MAJOR = 0
 BSA_V_DIM_MAJOR = 1
 
 # Every symbol include/bsattn.h declares.
-EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_perm_from_labels",
+EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_crm_build", "bsa_crm_row_ptr",
+           "bsa_crm_to_csr", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
            "bsa_attn_fwd",
            "bsa_device_cus", "bsa_device_clock_khz")
@@ -38,6 +39,7 @@ class AttnArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("causal", I32),
         ("v_layout", I32),
+        ("crm", P),
     ]
 
 
@@ -69,6 +71,12 @@ def load():
         L.bsa_csr_fill.restype = ctypes.c_int
         L.bsa_csr_fill.argtypes = [P, P, ctypes.c_float, P, I64, I32, I32, ctypes.c_int, P, P, P,
                                    I64, P]
+        L.bsa_crm_build.restype = ctypes.c_int
+        L.bsa_crm_build.argtypes = [P, P, ctypes.c_float, I64, I32, I32, ctypes.c_int, P, P]
+        L.bsa_crm_row_ptr.restype = ctypes.c_int
+        L.bsa_crm_row_ptr.argtypes = [P, I64, I32, P, ctypes.POINTER(I64), P]
+        L.bsa_crm_to_csr.restype = ctypes.c_int
+        L.bsa_crm_to_csr.argtypes = [P, I64, I32, P, P, I64, P]
         L.bsa_perm_from_labels.restype = ctypes.c_int
         L.bsa_perm_from_labels.argtypes = [P, I64, I64, I32, P, P]
         for fn in (L.bsa_permute_rows, L.bsa_unpermute_rows):

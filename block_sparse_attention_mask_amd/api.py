@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import AttnArgs, I64, I64x3, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
-           "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus"]
+           "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus", "crm_build",
+           "crm_row_ptr", "crm_to_csr"]
 
 _BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
 
@@ -110,6 +111,58 @@ def build_csr(mask=None, T=None, p: float = 0.0, lw_map=None, nQB: Optional[int]
     return row_ptr, col, lw
 
 
+def crm_build(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,
+              crm: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bsa_crm_build -> CRM rows, int32 [R][ceil(nKB / 32)] holding the uint32 words."""
+    src = mask if mask is not None else T
+    R, nKB = src.shape
+    nQB = nKB if nQB is None else nQB
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+    if T is not None:
+        _dev(T, "T", torch.float32)
+    if not src.is_contiguous():
+        raise ValueError("mask / T must be contiguous [R][nKB]")
+    W = (nKB + 31) // 32
+    if crm is None:
+        crm = torch.empty((R, W), dtype=torch.int32, device=src.device)
+    elif crm.numel() < R * W or not crm.is_contiguous():
+        raise ValueError("crm must be a contiguous buffer of R * ceil(nKB / 32) words")
+    check("bsa_crm_build", load().bsa_crm_build(_ptr(mask), _ptr(T), float(p), R, nQB, nKB, int(force_diag),
+                                                _ptr(crm), _stream(stream)))
+    return crm
+
+
+def _crm_rows(crm: torch.Tensor, nKB: int) -> int:
+    _dev(crm, "crm", (torch.int32, torch.uint32))
+    W = (nKB + 31) // 32
+    if not crm.is_contiguous() or crm.numel() % W:
+        raise ValueError("crm must be contiguous [R][ceil(nKB / 32)]")
+    return crm.numel() // W
+
+
+def crm_row_ptr(crm: torch.Tensor, nKB: int, row_ptr: Optional[torch.Tensor] = None, want_nnz: bool = True,
+                stream=None):
+    """bsa_crm_row_ptr -> (row_ptr int32 [R+1], nnz or None)."""
+    R = _crm_rows(crm, nKB)
+    if row_ptr is None:
+        row_ptr = torch.empty(R + 1, dtype=torch.int32, device=crm.device)
+    nnz = I64(0)
+    check("bsa_crm_row_ptr", load().bsa_crm_row_ptr(_ptr(crm), R, nKB, _ptr(row_ptr),
+                                                    ctypes.byref(nnz) if want_nnz else None, _stream(stream)))
+    return row_ptr, (int(nnz.value) if want_nnz else None)
+
+
+def crm_to_csr(crm: torch.Tensor, nKB: int, row_ptr: torch.Tensor, nnz: int, col=None, stream=None):
+    """bsa_crm_to_csr -> col int32 [nnz] (ascending per row)."""
+    R = _crm_rows(crm, nKB)
+    if col is None:
+        col = torch.empty(max(nnz, 1), dtype=torch.int32, device=crm.device)
+    check("bsa_crm_to_csr", load().bsa_crm_to_csr(_ptr(crm), R, nKB, _ptr(row_ptr), _ptr(col), col.numel(),
+                                                  _stream(stream)))
+    return col[:nnz]
+
+
 def perm_from_labels(labels: torch.Tensor, n_clusters: int, perm=None, stream=None) -> torch.Tensor:
     _dev(labels, "labels", torch.int32)
     labels = labels.contiguous()
@@ -190,15 +243,16 @@ def spectral_order(row_ptr: torch.Tensor, col: torch.Tensor, BH: int, nQB: int, 
     return perm, angle
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
-             col: torch.Tensor, block: int, lw: Optional[torch.Tensor] = None,
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optional[torch.Tensor],
+             col: Optional[torch.Tensor], block: int, lw: Optional[torch.Tensor] = None,
              order: Optional[torch.Tensor] = None, scatter_perm_q: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = False, scale: float = 0.0, causal: bool = False,
-             v_dim_major: bool = False, stream=None):
+             v_dim_major: bool = False, crm: Optional[torch.Tensor] = None, stream=None):
     """Block-sparse attention forward; returns (out, lse or None).  With
     ``v_dim_major`` v is [B][Hkv][d][ld] (keys contiguous, from transpose_rows),
-    otherwise [B][Hkv][N][d]."""
+    otherwise [B][Hkv][N][d].  With ``crm`` (CRM rows from crm_build) the lists
+    come from the bitmask words and row_ptr/col may be None."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     B, Hq, N, d = q.shape
@@ -219,5 +273,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.T
     a.scale = float(scale)
     a.causal = int(bool(causal))
     a.v_layout = _lib.BSA_V_DIM_MAJOR if v_dim_major else _lib.BSA_V_TOKEN_MAJOR
+    if crm is not None:
+        nQB = -(-N // int(block))
+        if _crm_rows(crm, nQB) != B * Hq * nQB:
+            raise ValueError("crm must hold B * Hq * ceil(N / block) rows")
+    a.crm = _ptr(crm)
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse

@@ -21,6 +21,9 @@ struct AttnParams {
   // token-major, (batch, head, head-dim row) when dim-major
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
   const int32_t *row_ptr, *col;
+  const uint32_t *crm;   // CRM rows in place of row_ptr/col (kernels instantiated for it)
+  int crm_words;         // words per CRM row
+  uint32_t crm_tail;     // bits of a row's last word that name KV blocks
   const float *lw;
   const int32_t *order;
   const int32_t *sperm;

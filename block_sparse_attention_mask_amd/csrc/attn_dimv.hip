@@ -58,7 +58,7 @@ struct DCfg {
   static_assert(NQG <= 4, "one merge buffer per query group");
 };
 
-template <int BLK, int D>
+template <int BLK, int D, bool kCrm>
 __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_t *__restrict__ row_ptr,
                                                const int32_t *__restrict__ col, const float *__restrict__ lw,
                                                const int32_t *__restrict__ order,
@@ -87,7 +87,18 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   const int g = h / p.G;
   // every per-head extent is below 2^30 bytes, so token positions fit in 32 bits
   const int N = (int)p.N;
-  const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
+  // the row's list: entries [e0, e1) of col, or positions [0, e1) of the
+  // walk over the row's CRM words
+  int e0, e1;
+  const uint32_t *crow = nullptr;
+  if constexpr (kCrm) {
+    crow = p.crm + (int64_t)r * p.crm_words;
+    e0 = 0;
+    e1 = __builtin_amdgcn_readfirstlane(bsa_crm_count(crow, p.crm_words, p.crm_tail, lane));
+  } else {
+    e0 = row_ptr[r];
+    e1 = row_ptr[r + 1];
+  }
   // KV blocks at or after mlim need the element mask: the partial last block
   // and, when causal, blocks from the diagonal on
   const int nfull = N / BLK;
@@ -258,9 +269,14 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
 
   for (int c0 = e0; c0 < e1; c0 += C::LIST) {
     const int n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
-    for (int i = tid; i < n; i += C::NT) {
-      lcol[i] = col[c0 + i];
-      lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
+    if constexpr (kCrm) {
+      bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
+      for (int i = tid; i < n; i += C::NT) lbias[i] = 0.f;
+    } else {
+      for (int i = tid; i < n; i += C::NT) {
+        lcol[i] = col[c0 + i];
+        lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
+      }
     }
     __syncthreads();
     // prologue: K(0), V(0), K(1) resident, then S(0)
@@ -333,19 +349,21 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   }
 }
 
-// One plain kernel per tile shape (the body is a force-inlined template).
-#define BSA_DIMV_KERNEL(BLK, D)                                                                     \
+// One plain kernel per tile shape and list format (the body is a
+// force-inlined template).
+#define BSA_DIMV_KERNEL(NAME, BLK, D, CRM)                                                          \
   __global__ __attribute__((amdgpu_flat_work_group_size(4 * BLK, 4 * BLK), amdgpu_waves_per_eu(2, 2))) \
-  void attn_dimv_##BLK##_##D(const AttnParams p, const int32_t *__restrict__ row_ptr,              \
-                             const int32_t *__restrict__ col, const float *__restrict__ lw,          \
-                             const int32_t *__restrict__ order, const int32_t *__restrict__ sperm,   \
-                             uint16_t *__restrict__ out, float *__restrict__ lse) {                  \
-    attn_dimv_body<BLK, D>(p, row_ptr, col, lw, order, sperm, out, lse);                           \
+  void NAME(const AttnParams p, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col, \
+            const float *__restrict__ lw, const int32_t *__restrict__ order,                         \
+            const int32_t *__restrict__ sperm, uint16_t *__restrict__ out, float *__restrict__ lse) { \
+    attn_dimv_body<BLK, D, CRM>(p, row_ptr, col, lw, order, sperm, out, lse);                      \
   }
-BSA_DIMV_KERNEL(128, 128)
-BSA_DIMV_KERNEL(128, 64)
-BSA_DIMV_KERNEL(64, 128)
-BSA_DIMV_KERNEL(64, 64)
+BSA_DIMV_KERNEL(attn_dimv_128_128, 128, 128, false)
+BSA_DIMV_KERNEL(attn_dimv_128_64, 128, 64, false)
+BSA_DIMV_KERNEL(attn_dimv_64_128, 64, 128, false)
+BSA_DIMV_KERNEL(attn_dimv_64_64, 64, 64, false)
+BSA_DIMV_KERNEL(attn_dimv_crm_64_128, 64, 128, true)
+BSA_DIMV_KERNEL(attn_dimv_crm_64_64, 64, 64, true)
 #undef BSA_DIMV_KERNEL
 
 }  // namespace dimv
@@ -353,7 +371,11 @@ BSA_DIMV_KERNEL(64, 64)
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), t(4 * block);
 #define BSA_ARGS p, p.row_ptr, p.col, p.lw, p.order, p.sperm, p.o, p.lse
-  if (block == 128 && d == 128) hipLaunchKernelGGL(dimv::attn_dimv_128_128, g, t, 0, s, BSA_ARGS);
+  if (p.crm) {
+    if (block != 64) return hipErrorInvalidValue;
+    if (d == 128) hipLaunchKernelGGL(dimv::attn_dimv_crm_64_128, g, t, 0, s, BSA_ARGS);
+    else hipLaunchKernelGGL(dimv::attn_dimv_crm_64_64, g, t, 0, s, BSA_ARGS);
+  } else if (block == 128 && d == 128) hipLaunchKernelGGL(dimv::attn_dimv_128_128, g, t, 0, s, BSA_ARGS);
   else if (block == 128) hipLaunchKernelGGL(dimv::attn_dimv_128_64, g, t, 0, s, BSA_ARGS);
   else if (d == 128) hipLaunchKernelGGL(dimv::attn_dimv_64_128, g, t, 0, s, BSA_ARGS);
   else hipLaunchKernelGGL(dimv::attn_dimv_64_64, g, t, 0, s, BSA_ARGS);

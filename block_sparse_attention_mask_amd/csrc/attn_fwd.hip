@@ -1,6 +1,7 @@
 // bsa_attn_fwd: argument checks and dispatch to the attention kernels
 // (dim-major V: attn_pp.hip for 128-key blocks, attn_dimv.hip for 64;
-// token-major V: attn_tokv.hip).
+// token-major V: attn_tokv.hip).  Lists come as CSR or as CRM rows; the
+// dim-major kernels have a variant for each.
 #include "attn_common.h"
 
 namespace {
@@ -15,12 +16,15 @@ bool bad_strides(const int64_t s[3]) {
 
 extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   if (!a) return BSA_ERR_ARG;
-  if (!a->q || !a->k || !a->v || !a->o || !a->row_ptr || !a->col) return BSA_ERR_ARG;
+  if (!a->q || !a->k || !a->v || !a->o) return BSA_ERR_ARG;
+  if (!a->crm && (!a->row_ptr || !a->col)) return BSA_ERR_ARG;
   if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->N <= 0 || a->n_order < 0) return BSA_ERR_ARG;
   if (a->Hq % a->Hkv) return BSA_ERR_ARG;
   if (a->v_layout != BSA_V_TOKEN_MAJOR && a->v_layout != BSA_V_DIM_MAJOR) return BSA_ERR_ARG;
   if ((a->d != 64 && a->d != 128) || (a->block != 64 && a->block != 128)) return BSA_ERR_UNSUPPORTED;
   if (a->causal && a->scatter_perm_q) return BSA_ERR_UNSUPPORTED;
+  // CRM rows feed the dim-major kernels and carry no log-weights
+  if (a->crm && (a->lw || a->v_layout != BSA_V_DIM_MAJOR)) return BSA_ERR_UNSUPPORTED;
   if (!bsa_aligned16(a->q) || !bsa_aligned16(a->k) || !bsa_aligned16(a->v) || !bsa_aligned16(a->o))
     return BSA_ERR_ARG;
   if (bad_strides(a->q_str) || bad_strides(a->k_str) || bad_strides(a->v_str) || bad_strides(a->o_str))
@@ -57,6 +61,9 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   p.os0 = a->o_str[0]; p.os1 = a->o_str[1]; p.os2 = a->o_str[2];
   p.row_ptr = a->row_ptr;
   p.col = a->col;
+  p.crm = a->crm;
+  p.crm_words = bsa_crm_words((int)nQB);
+  p.crm_tail = bsa_crm_tail((int)nQB);
   p.lw = a->lw;
   p.order = a->order;
   p.sperm = a->scatter_perm_q;

@@ -44,6 +44,10 @@
 //     O and l rescaled and the tile's exponentials redone, only when a
 //     lane's 32 probabilities of the tile sum past 32 * 2^8 (so some
 //     probability exceeded 2^8) or nothing has been accumulated yet.
+//   * The row's list is staged in LDS, up to 1024 entries at a time: copied
+//     from the CSR column array, or walked out of the row's CRM words
+//     (ScalingAttention, section 7.3) with each wavefront taking a 4-bit
+//     slice of every word.
 //   * K tile offsets go into the range-checked lane offset, so rows at or
 //     past N of a partial last block read as zeros; V^T rows hold every key
 //     of every block, so their tile offset is scalar.
@@ -76,7 +80,7 @@ struct PCfg {
   static_assert(64 * DT * 16 * 4 <= KB, "merge data of a query group fits a K buffer");
 };
 
-template <int D>
+template <int D, bool kCrm>
 __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t *__restrict__ row_ptr,
                                              const int32_t *__restrict__ col, const float *__restrict__ lw,
                                              const int32_t *__restrict__ order,
@@ -103,7 +107,18 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   const int g = h / p.G;
   // every per-head extent is below 2^30 bytes, so token positions fit in 32 bits
   const int N = (int)p.N;
-  const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
+  // the row's list: entries [e0, e1) of col, or positions [0, e1) of the
+  // walk over the row's CRM words
+  int e0, e1;
+  const uint32_t *crow = nullptr;
+  if constexpr (kCrm) {
+    crow = p.crm + (int64_t)r * p.crm_words;
+    e0 = 0;
+    e1 = __builtin_amdgcn_readfirstlane(bsa_crm_count(crow, p.crm_words, p.crm_tail, lane));
+  } else {
+    e0 = row_ptr[r];
+    e1 = row_ptr[r + 1];
+  }
   // KV blocks at or after mlim need the element mask: the partial last block
   // and, when causal, blocks from the diagonal on
   const int nfull = N / C::BLK;
@@ -400,9 +415,14 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
 
     for (int c0 = e0; c0 < e1; c0 += C::LIST) {
       n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
-      for (int i = tid; i < n; i += C::NT) {
-        lcol[i] = col[c0 + i];
-        lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
+      if constexpr (kCrm) {
+        bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
+        for (int i = tid; i < n; i += C::NT) lbias[i] = 0.f;
+      } else {
+        for (int i = tid; i < n; i += C::NT) {
+          lcol[i] = col[c0 + i];
+          lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
+        }
       }
       __syncthreads();
       // what the first phases read: K entries 0 and 1 and V^T entry 0 of half
@@ -469,16 +489,18 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   else half(std::integral_constant<int, 1>());
 }
 
-#define BSA_PP_KERNEL(D)                                                                            \
+// One plain kernel per head dim and list format (CSR, or CRM words).
+#define BSA_PP_KERNEL(NAME, D, CRM)                                                                 \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))     \
-  void attn_pp_128_##D(const AttnParams p, const int32_t *__restrict__ row_ptr,                    \
-                       const int32_t *__restrict__ col, const float *__restrict__ lw,                \
-                       const int32_t *__restrict__ order, const int32_t *__restrict__ sperm,         \
-                       uint16_t *__restrict__ out, float *__restrict__ lse) {                        \
-    attn_pp_body<D>(p, row_ptr, col, lw, order, sperm, out, lse);                                  \
+  void NAME(const AttnParams p, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col, \
+            const float *__restrict__ lw, const int32_t *__restrict__ order,                         \
+            const int32_t *__restrict__ sperm, uint16_t *__restrict__ out, float *__restrict__ lse) { \
+    attn_pp_body<D, CRM>(p, row_ptr, col, lw, order, sperm, out, lse);                             \
   }
-BSA_PP_KERNEL(128)
-BSA_PP_KERNEL(64)
+BSA_PP_KERNEL(attn_pp_128_128, 128, false)
+BSA_PP_KERNEL(attn_pp_128_64, 64, false)
+BSA_PP_KERNEL(attn_pp_crm_128_128, 128, true)
+BSA_PP_KERNEL(attn_pp_crm_128_64, 64, true)
 #undef BSA_PP_KERNEL
 
 }  // namespace pp
@@ -486,8 +508,14 @@ BSA_PP_KERNEL(64)
 hipError_t launch_attn_pp(const AttnParams &p, int d, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), t(512);
 #define BSA_ARGS p, p.row_ptr, p.col, p.lw, p.order, p.sperm, p.o, p.lse
-  if (d == 128) hipLaunchKernelGGL(pp::attn_pp_128_128, g, t, 0, s, BSA_ARGS);
-  else hipLaunchKernelGGL(pp::attn_pp_128_64, g, t, 0, s, BSA_ARGS);
+  if (p.crm) {
+    if (d == 128) hipLaunchKernelGGL(pp::attn_pp_crm_128_128, g, t, 0, s, BSA_ARGS);
+    else hipLaunchKernelGGL(pp::attn_pp_crm_128_64, g, t, 0, s, BSA_ARGS);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(pp::attn_pp_128_128, g, t, 0, s, BSA_ARGS);
+  } else {
+    hipLaunchKernelGGL(pp::attn_pp_128_64, g, t, 0, s, BSA_ARGS);
+  }
 #undef BSA_ARGS
   return hipGetLastError();
 }

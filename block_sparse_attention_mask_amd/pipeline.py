@@ -1,6 +1,7 @@
 """One pass of the whole block-sparse attention path on device tensors:
 
-mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill)
+mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill), or CRM rows
+   (bsa_crm_build) with row offsets from their popcounts (bsa_crm_row_ptr)
 -> [cluster labels -> permutations; gather Q, K]        (permuted workloads)
 -> V gathered (when permuted) and written dim-major (bsa_transpose_rows)
 -> row schedule (bsa_schedule)
@@ -63,22 +64,33 @@ class StepResult:
     out: torch.Tensor
     lse: Optional[torch.Tensor]
     row_ptr: torch.Tensor
-    col: torch.Tensor
+    col: Optional[torch.Tensor]
     lw: Optional[torch.Tensor]
     order: Optional[torch.Tensor]
     perm_q: Optional[torch.Tensor] = None
     perm_k: Optional[torch.Tensor] = None
+    crm: Optional[torch.Tensor] = None
 
 
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
-            v_dim_major: bool = True, stream=None, stage1_iters: int = 0) -> StepResult:
+            v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  With
     ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
-    each head's query blocks (that many subspace iterations)."""
-    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag,
-                                     stream=stream)
+    each head's query blocks (that many subspace iterations).  With ``crm``
+    the lists are CRM rows (no log-weights, dim-major V); their sizes are
+    known up front, so this path makes no host synchronisation."""
+    crm_rows = None
+    if crm:
+        if dw.lw_map is not None or not v_dim_major:
+            raise ValueError("CRM lists carry no log-weights and need dim-major V")
+        crm_rows = api.crm_build(dw.mask, dw.T, dw.p, dw.nQB, dw.force_diag, stream=stream)
+        row_ptr, _ = api.crm_row_ptr(crm_rows, dw.nQB, want_nnz=False, stream=stream)
+        col = lw = None
+    else:
+        row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag,
+                                         stream=stream)
     q, k, v = dw.q, dw.k, dw.v
     perm_q = perm_k = None
     if dw.permuted:
@@ -94,7 +106,11 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     if schedule:
         row_perm = None
         if stage1_iters > 0:
-            row_perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, stage1_iters,
+            cols = col
+            if crm:
+                _, nnz = api.crm_row_ptr(crm_rows, dw.nQB, row_ptr=row_ptr, stream=stream)
+                cols = api.crm_to_csr(crm_rows, dw.nQB, row_ptr, nnz, stream=stream)
+            row_perm, _ = api.spectral_order(row_ptr, cols, dw.B * dw.Hq, dw.nQB, dw.nQB, stage1_iters,
                                              stream=stream)
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
                              row_perm=row_perm)
@@ -103,7 +119,8 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     if attn_events is not None:
         attn_events[0].record(s)
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
-                            want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, stream=stream)
+                            want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, crm=crm_rows,
+                            stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if dw.permuted and not fuse_scatter:
@@ -112,4 +129,4 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows)

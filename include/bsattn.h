@@ -91,6 +91,44 @@ int bsa_csr_fill(const uint8_t *mask, const float *T, float p, const float *lw_m
                  float *lw, int64_t capacity, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Mask -> CRM rows.
+ *
+ * Source: ScalingAttention, section 7.2 (Compressed Row Mask: each row is an
+ * aligned array of uint32 words, one bit per KV block, so one word load
+ * decodes 32 block states).
+ *
+ * Same keep rule and mask/T/p/force_diag arguments as bsa_csr_count.  Writes
+ * crm[r * W + v / 32] bit (v % 32) = 1 when entry (r, v) is kept, with
+ * W = ceil(nKB / 32); bits for v >= nKB are written as 0.  crm: device
+ * uint32 [R][W], caller-owned.  Errors as bsa_csr_count (crm == NULL is
+ * BSA_ERR_ARG).  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_crm_build(const uint8_t *mask, const float *T, float p, int64_t R, int32_t nQB, int32_t nKB,
+                  int force_diag, uint32_t *crm, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * CRM rows -> CSR row offsets: row_ptr[0] = 0, row_ptr[r + 1] = row_ptr[r] +
+ * popcount of row r (bits for v >= nKB are ignored).  crm: device uint32
+ * [R][ceil(nKB / 32)]; row_ptr: device int32 [R + 1] (output).  When
+ * nnz_out != NULL, stores row_ptr[R] there (host) and synchronises `stream`;
+ * otherwise asynchronous.  BSA_ERR_ARG for NULL pointers or negative sizes,
+ * BSA_ERR_UNSUPPORTED when R * nKB >= 2^31.
+ * ------------------------------------------------------------------------- */
+int bsa_crm_row_ptr(const uint32_t *crm, int64_t R, int32_t nKB, int32_t *row_ptr, int64_t *nnz_out,
+                    bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * CRM rows -> CSR column lists by the forward iterator of ScalingAttention,
+ * section 7.3 (Algorithm 2: ascending walk by count-trailing-zeros and
+ * clear-lowest-bit).  row_ptr as bsa_crm_row_ptr produced it; writes
+ * col[row_ptr[r] ..] = the blocks of row r in ascending order.  Entries at an
+ * index >= capacity are never written.  BSA_ERR_ARG for NULL pointers,
+ * negative sizes or capacity < 0.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_crm_to_csr(const uint32_t *crm, int64_t R, int32_t nKB, const int32_t *row_ptr, int32_t *col,
+                   int64_t capacity, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Cluster labels -> gather permutation.
  *
  * Source: permuted block-sparse attention clusters queries and keys and
@@ -215,7 +253,13 @@ int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int
  * of the query at position i is written to position scatter_perm_q[bh][i] of
  * o (and lse), i.e. the inverse permutation is fused into the store.
  * scale <= 0 selects 1/sqrt(d).  A row with an empty list writes O = 0 and
- * LSE = -inf.  Log-weights must be finite or -inf.  Asynchronous.
+ * LSE = -inf.  Log-weights must be finite or -inf.  crm (optional, device
+ * uint32 [R][ceil(nQB/32)], the layout of bsa_crm_build): when set, each
+ * row's list is the ascending walk of its CRM words (ScalingAttention,
+ * section 7.3) and row_ptr/col are not read (may be NULL); it requires
+ * v_layout = BSA_V_DIM_MAJOR and lw = NULL (else BSA_ERR_UNSUPPORTED).
+ * Results are bit-identical to the CSR lists the same mask gives.
+ * Asynchronous.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void *q, *k, *v;
@@ -232,6 +276,7 @@ typedef struct {
   float scale;
   int32_t causal;
   int32_t v_layout; /* BSA_V_TOKEN_MAJOR or BSA_V_DIM_MAJOR */
+  const uint32_t *crm; /* CRM rows in place of row_ptr/col, or NULL */
 } bsa_attn_args;
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);

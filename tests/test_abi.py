@@ -99,6 +99,22 @@ def test_spectral_order_argument_errors(L):
     assert L.bsa_spectral_order(FAKE, FAKE, 4, 700, 700, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
 
 
+def test_crm_argument_errors(L):
+    n = _lib.I64(0)
+    assert L.bsa_crm_build(None, None, 0.5, 4, 2, 2, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_build(FAKE, FAKE, 0.5, 4, 2, 2, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_build(FAKE, None, 0.5, 4, 2, 2, 1, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_build(FAKE, None, 0.5, 4, 2, 0, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_build(FAKE, None, 0.5, 1 << 30, 4, 4, 1, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_crm_row_ptr(FAKE, 4, 40, None, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_row_ptr(None, 4, 40, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_row_ptr(FAKE, -1, 40, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_row_ptr(FAKE, 1 << 30, 40, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_crm_to_csr(FAKE, 4, 40, FAKE, None, 3, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_to_csr(FAKE, 4, 40, FAKE, FAKE, -1, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_crm_to_csr(FAKE, 4, 0, FAKE, FAKE, 3, None) == _lib.BSA_ERR_ARG
+
+
 def _args(**kw):
     a = _lib.AttnArgs()
     a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
@@ -128,6 +144,10 @@ def _args(**kw):
     (dict(v_layout=1, v_str=_lib.I64x3(128 * 1000, 128 * 1000, 1000)), _lib.BSA_ERR_ARG),   # rows < 1024 keys
     (dict(v_layout=1, N=1 << 20, q_str=_lib.I64x3(0, 0, 1024), v_str=_lib.I64x3(0, 0, 1 << 20)),
      _lib.BSA_ERR_UNSUPPORTED),                                                              # 32-bit offsets
+    (dict(crm=FAKE, lw=FAKE, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024)),
+     _lib.BSA_ERR_UNSUPPORTED),                                                              # CRM has no weights
+    (dict(crm=FAKE), _lib.BSA_ERR_UNSUPPORTED),                                              # CRM: dim-major V only
+    (dict(crm=None, col=None), _lib.BSA_ERR_ARG),
 ])
 def test_attn_argument_errors(L, kw, code):
     a = _args(**kw)
