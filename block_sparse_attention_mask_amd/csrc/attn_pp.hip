@@ -114,7 +114,10 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   if constexpr (kCrm) {
     crow = p.crm + (int64_t)r * p.crm_words;
     e0 = 0;
-    e1 = __builtin_amdgcn_readfirstlane(bsa_crm_count(crow, p.crm_words, p.crm_tail, lane));
+    // the first chunk is walked here; a row shorter than a chunk needs no
+    // separate count
+    const int seen = bsa_crm_walk(crow, p.crm_words, p.crm_tail, 0, C::LIST, lcol, wave, C::NW, lane);
+    e1 = __builtin_amdgcn_readfirstlane(seen < C::LIST ? seen : bsa_crm_count(crow, p.crm_words, p.crm_tail, lane));
   } else {
     e0 = row_ptr[r];
     e1 = row_ptr[r + 1];
@@ -416,7 +419,7 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     for (int c0 = e0; c0 < e1; c0 += C::LIST) {
       n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
       if constexpr (kCrm) {
-        bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
+        if (c0 > 0) bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
         for (int i = tid; i < n; i += C::NT) lbias[i] = 0.f;
       } else {
         for (int i = tid; i < n; i += C::NT) {

@@ -68,23 +68,26 @@ __device__ __forceinline__ int bsa_crm_count(const uint32_t *row, int W, uint32_
 // wavefront walks the bits of its word that `part`/`nparts` selects (a
 // contiguous 32/nparts-bit slice, so nparts wavefronts together cover the
 // word) by count-trailing-zeros and clear-lowest-bit.  Every wavefront of a
-// group must call it with the same arguments except `part`.
-__device__ __forceinline__ void bsa_crm_walk(const uint32_t *row, int W, uint32_t tail, int64_t c0, int lim,
-                                             int32_t *dst, int part, int nparts, int lane) {
+// group must call it with the same arguments except `part`.  Returns the
+// number of blocks it passed over: the row's length whenever that is below
+// c0 + lim (the walk stops at the first word batch that reaches c0 + lim).
+__device__ __forceinline__ int bsa_crm_walk(const uint32_t *row, int W, uint32_t tail, int c0, int lim,
+                                            int32_t *dst, int part, int nparts, int lane) {
   const int sb = 32 / nparts;
   const uint32_t below = (1u << (sb * part)) - 1u;
   const uint32_t mine = (sb == 32 ? ~0u : (1u << sb) - 1u) << (sb * part);
-  int64_t run = 0;   // list position of the batch's first block
+  int run = 0;   // list position of the batch's first block
   for (int w0 = 0; w0 < W && run < c0 + lim; w0 += 64) {
     const int w = w0 + lane;
     const uint32_t x = bsa_crm_word(row, w, W, tail);
     const int cnt = __popc(x);
     const int incl = bsa_wave_incl_scan(cnt, lane);
-    int64_t pos = run + (incl - cnt) + __popc(x & below);
+    int pos = run + (incl - cnt) + __popc(x & below);
     for (uint32_t y = x & mine; y; y &= y - 1u, ++pos) {
-      const int64_t i = pos - c0;
+      const int i = pos - c0;
       if (i >= 0 && i < lim) dst[i] = 32 * w + __builtin_ctz(y);
     }
     run += __shfl(incl, 63, 64);
   }
+  return run;
 }
