@@ -181,7 +181,7 @@ def attn_kernel_name(block, d):
     return ("attn_pp_128_%d" % d) if block == 128 else ("attn_dimv_%d_%d" % (block, d))
 
 
-ATTN_SOURCES = ("attn_pp.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip")
+ATTN_SOURCES = ("attn_pp.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip", "bsa_internal.h")
 
 
 def attn_sources_sha256():
