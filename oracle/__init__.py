@@ -46,6 +46,13 @@ def lib():
         L.oracle_build_crm.argtypes = [P, P, ctypes.c_float, I64, I64, I64, ctypes.c_int, P]
         L.oracle_crm_walk.restype = I64
         L.oracle_crm_walk.argtypes = [P, I64, I64, P, P, I64]
+        L.oracle_segment_offsets.restype = ctypes.c_int
+        L.oracle_segment_offsets.argtypes = [P, I64, I64, ctypes.c_int32, P]
+        L.oracle_segment_means.restype = ctypes.c_int
+        L.oracle_segment_means.argtypes = [P, P, I64, I64, I64, I64, P, ctypes.c_int32, ctypes.c_int32, P]
+        L.oracle_is_sample.restype = ctypes.c_int
+        L.oracle_is_sample.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int32, I64, ctypes.c_int32, I64,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P, P]
         L.oracle_perm_from_labels.restype = ctypes.c_int
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
@@ -115,6 +122,61 @@ def crm_walk(words: np.ndarray, nKB: int):
     n2 = lib().oracle_crm_walk(_p(words), R, nKB, _p(row_ptr), _p(col), n)
     assert n2 == n
     return row_ptr, col[:n]
+
+
+def segment_offsets(labels: np.ndarray, G: int) -> np.ndarray:
+    """seg_ptr int32 [BH][G+1]: tokens of each head with label < g."""
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    BH, N = labels.shape
+    sp = np.empty((BH, G + 1), dtype=np.int32)
+    rc = lib().oracle_segment_offsets(_p(labels), BH, N, int(G), _p(sp))
+    if rc:
+        raise ValueError("oracle_segment_offsets failed: %d" % rc)
+    return sp
+
+
+def segment_means(x, seg_ptr=None, G: int = 0, seg_len: int = 0) -> np.ndarray:
+    """x [B][H][N][d] uint16 bf16 bits (contiguous last dim).  Segments from
+    seg_ptr [B*H][G+1], or fixed-length seg_len.  Returns float32 [B*H][G][d]."""
+    x = np.asarray(x)
+    assert x.dtype == np.uint16 and x.strides[-1] == 2
+    B, H, N, d = x.shape
+    if seg_ptr is not None:
+        seg_ptr = np.ascontiguousarray(seg_ptr, dtype=np.int32)
+        G = seg_ptr.shape[1] - 1
+    else:
+        G = -(-N // seg_len)
+    xs = np.array([s // 2 for s in x.strides[:3]], dtype=np.int64)
+    out = np.empty((B * H, G, d), dtype=np.float32)
+    rc = lib().oracle_segment_means(_p(x), _p(xs), B, H, N, d, _p(seg_ptr), int(G), int(seg_len), _p(out))
+    if rc:
+        raise ValueError("oracle_segment_means failed: %d" % rc)
+    return out
+
+
+def is_sample(qbar, kbar, q_seg_ptr, uoff, B: int, Hq: int, Hkv: int, N: int, block: int, m_exact: int,
+              m_sample: int, scale: Optional[float] = None):
+    """Group-shared importance sampling over KV tiles.  qbar float32
+    [B*Hq][G][d], kbar float32 [B*Hkv][nKB][d], q_seg_ptr int32 [B*Hq][G+1],
+    uoff float64 [B*Hq][G].  Returns (mask uint8 [R][nKB], lw_map float32
+    [R][nKB], pi float64 [B*Hq][G][nKB])."""
+    qbar = np.ascontiguousarray(qbar, dtype=np.float32)
+    kbar = np.ascontiguousarray(kbar, dtype=np.float32)
+    q_seg_ptr = np.ascontiguousarray(q_seg_ptr, dtype=np.int32)
+    uoff = np.ascontiguousarray(uoff, dtype=np.float64)
+    G, d = qbar.shape[1], qbar.shape[2]
+    nb = -(-N // block)
+    assert kbar.shape == (B * Hkv, nb, d) and q_seg_ptr.shape == (B * Hq, G + 1) and uoff.shape == (B * Hq, G)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    mask = np.empty((B * Hq * nb, nb), dtype=np.uint8)
+    lw = np.empty((B * Hq * nb, nb), dtype=np.float32)
+    pi = np.empty((B * Hq, G, nb), dtype=np.float64)
+    rc = lib().oracle_is_sample(_p(qbar), _p(kbar), _p(q_seg_ptr), _p(uoff), B, Hq, Hkv, int(G), N, int(block), d,
+                                int(m_exact), int(m_sample), float(scale), _p(mask), _p(lw), _p(pi))
+    if rc:
+        raise ValueError("oracle_is_sample failed: %d" % rc)
+    return mask, lw, pi
 
 
 def perm_from_labels(labels: np.ndarray, n_clusters: int) -> np.ndarray:

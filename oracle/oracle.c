@@ -51,6 +51,17 @@
  *                     Eq. (1)-(3), with the per-block log-weight added to the
  *                     scaled logit (InstaGen Algorithm 1, Horvitz-Thompson
  *                     weights as log w).  Masked pairs are -inf.
+ *  oracle_segment_offsets / oracle_segment_means
+ *                     Centroids for InstaGen Algorithm 1 step 2: the tokens
+ *                     of each label form one contiguous segment of the
+ *                     label-sorted sequence, and a centroid is the mean of
+ *                     its segment's rows (fixed-length segments give the mean
+ *                     key of each 128-key tile).
+ *  oracle_is_sample   Group-shared importance sampling over KV tiles
+ *                     (InstaGen Algorithm 1 steps 2-13, section 3.2.1
+ *                     Eq. 4): centroid scores, the exact set by decreasing
+ *                     size x score, water-filled inclusion probabilities,
+ *                     a systematic PPS sample, Horvitz-Thompson log-weights.
  *  oracle_count_pairs Number of allowed (query, key) token pairs; the FLOP
  *                     convention of 4*d per pair is the one behind INTRA's
  *                     GFLOPS column (INTRA, Table 1 and the overhead table).
@@ -510,4 +521,194 @@ int64_t oracle_count_pairs(const int32_t *row_ptr, const int32_t *col, int64_t R
     }
   }
   return total;
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* centroids: segment offsets and segment means                              */
+/* ------------------------------------------------------------------------ */
+/* seg_ptr[bh][g] = number of tokens of head bh whose label is in [0, g), for
+ * g = 0..G (labels outside [0, G) are not counted: they sort after every
+ * valid label).  seg_ptr is [BH][G + 1]. */
+int oracle_segment_offsets(const int32_t *labels, int64_t BH, int64_t N, int32_t G, int32_t *seg_ptr) {
+  if (!labels || !seg_ptr || BH < 0 || N < 0 || G <= 0) return OR_ERR_ARG;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    int32_t *sp = seg_ptr + bh * (G + 1);
+    for (int32_t g = 0; g <= G; ++g) sp[g] = 0;
+    for (int64_t t = 0; t < N; ++t) {
+      int32_t l = labels[bh * N + t];
+      if (l >= 0 && l < G) sp[l + 1] += 1;
+    }
+    for (int32_t g = 0; g < G; ++g) sp[g + 1] += sp[g];
+  }
+  return OR_OK;
+}
+
+/* means[bh][s][:] = mean of the bf16 rows x[b][h][i][:] for i in segment s of
+ * head bh = (b, h): [seg_ptr[bh][s], seg_ptr[bh][s+1]) when seg_ptr != NULL,
+ * else [s * seg_len, min(N, (s+1) * seg_len)) with G = ceil(N / seg_len).
+ * Sums in fp64 in ascending i; an empty segment has mean 0.  xs: element
+ * strides (batch, head, token). */
+int oracle_segment_means(const uint16_t *x, const int64_t *xs, int64_t B, int64_t H, int64_t N, int64_t d,
+                         const int32_t *seg_ptr, int32_t G, int32_t seg_len, float *means) {
+  if (!x || !xs || !means || B < 0 || H < 0 || N < 0 || d <= 0 || G <= 0) return OR_ERR_ARG;
+  if (!seg_ptr && seg_len <= 0) return OR_ERR_ARG;
+  double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!acc) return OR_ERR_ARG;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h) {
+      int64_t bh = b * H + h;
+      for (int32_t s = 0; s < G; ++s) {
+        int64_t lo, hi;
+        if (seg_ptr) {
+          lo = seg_ptr[bh * (G + 1) + s];
+          hi = seg_ptr[bh * (G + 1) + s + 1];
+        } else {
+          lo = (int64_t)s * seg_len;
+          hi = lo + seg_len < N ? lo + seg_len : N;
+        }
+        for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int64_t i = lo; i < hi; ++i)
+          for (int64_t c = 0; c < d; ++c) acc[c] += bf16_to_double(x[b * xs[0] + h * xs[1] + i * xs[2] + c]);
+        float *m = means + (bh * G + s) * d;
+        for (int64_t c = 0; c < d; ++c) m[c] = hi > lo ? (float)(acc[c] / (double)(hi - lo)) : 0.0f;
+      }
+    }
+  free(acc);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* group-shared importance sampling over KV tiles                            */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  double mass;
+  int32_t v;
+} tile_mass;
+
+static int cmp_mass_desc(const void *a, const void *b) {
+  const tile_mass *x = (const tile_mass *)a, *y = (const tile_mass *)b;
+  if (x->mass != y->mass) return x->mass > y->mass ? -1 : 1;
+  return x->v < y->v ? -1 : (x->v > y->v);
+}
+
+/* For every head (b, h) and query group g (the query blocks u whose first
+ * token, u * block, lies in segment g of q_seg_ptr):
+ *   score:    a_v = scale * qbar[bh][g] . kbar[(b, h / (Hq/Hkv))][v], summed
+ *             in fp64 over ascending components; the tile's mass is
+ *             |v| * exp(a_v - max_v a_v), |v| its number of real keys (the
+ *             size x centroid-score product of step 4; the common factor
+ *             exp(-max) cancels in every step below);
+ *   exact:    the m_exact tiles of largest mass, ties to the lower v;
+ *   residual: the other tiles; pi = min(1, lam * mass) with sum m_sample
+ *             (Eq. 4), or pi = 1 for all when there are at most m_sample;
+ *   sample:   systematic PPS over the residual in ascending v: the points
+ *             u0 + k, k = 0..m_sample-1, u0 = uoff[bh][g] in [0, 1), fall
+ *             in the intervals [c_v, c_v + pi_v) of the running sum c;
+ *   weights:  exact and sampled tiles are kept; a sampled tile with pi < 1
+ *             gets lw = -ln(pi) (w = 1/pi, step 13), every other kept tile
+ *             and the diagonal tile lw = 0.
+ * mask/lw_map rows r = bh * nQB + u, [R][nKB], written in full (rows with no
+ * group are all zero).  pi_out (optional, [BH][G][nKB]): pi of residual
+ * tiles, 1 for exact tiles, 0 for groups with no query block. */
+int oracle_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_ptr, const double *uoff,
+                     int64_t B, int64_t Hq, int64_t Hkv, int32_t G, int64_t N, int32_t block, int64_t d,
+                     int32_t m_exact, int32_t m_sample, double scale, uint8_t *mask, float *lw_map,
+                     double *pi_out) {
+  if (!qbar || !kbar || !q_seg_ptr || !uoff || !mask || !lw_map) return OR_ERR_ARG;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || G <= 0 || N <= 0 || block <= 0 || d <= 0) return OR_ERR_ARG;
+  if (m_exact < 0 || m_sample < 0) return OR_ERR_ARG;
+  int64_t nb = (N + block - 1) / block;
+  memset(mask, 0, (size_t)(B * Hq * nb * nb));
+  memset(lw_map, 0, sizeof(float) * (size_t)(B * Hq * nb * nb));
+  if (pi_out) memset(pi_out, 0, sizeof(double) * (size_t)(B * Hq * G * nb));
+  double *a = (double *)malloc(sizeof(double) * (size_t)nb);
+  double *pi = (double *)malloc(sizeof(double) * (size_t)nb);
+  uint8_t *keep = (uint8_t *)malloc((size_t)nb);
+  uint8_t *exact = (uint8_t *)malloc((size_t)nb);
+  tile_mass *tm = (tile_mass *)malloc(sizeof(tile_mass) * (size_t)nb);
+  int rc = OR_OK;
+  if (!a || !pi || !keep || !exact || !tm) rc = OR_ERR_ARG;
+  for (int64_t bh = 0; rc == OR_OK && bh < B * Hq; ++bh) {
+    int64_t b = bh / Hq, h = bh % Hq, gk = b * Hkv + h / (Hq / Hkv);
+    for (int32_t g = 0; g < G; ++g) {
+      int64_t s0 = q_seg_ptr[bh * (G + 1) + g], s1 = q_seg_ptr[bh * (G + 1) + g + 1];
+      int64_t u0 = (s0 + block - 1) / block, u1 = (s1 + block - 1) / block;   /* u * block in [s0, s1) */
+      if (u1 > nb) u1 = nb;
+      if (u0 >= u1) continue;
+      /* step 2: centroid scores, and the tile masses */
+      const float *qg = qbar + (bh * G + g) * d;
+      double amax = -INFINITY;
+      for (int64_t v = 0; v < nb; ++v) {
+        const float *kv = kbar + (gk * nb + v) * d;
+        double s = 0.0;
+        for (int64_t c = 0; c < d; ++c) s += (double)qg[c] * (double)kv[c];
+        a[v] = scale * s;
+        if (a[v] > amax) amax = a[v];
+      }
+      for (int64_t v = 0; v < nb; ++v) {
+        int64_t size = N - v * block < block ? N - v * block : block;
+        tm[v].mass = (double)size * exp(a[v] - amax);
+        tm[v].v = (int32_t)v;
+      }
+      /* step 4: exact set */
+      qsort(tm, (size_t)nb, sizeof(tile_mass), cmp_mass_desc);
+      memset(exact, 0, (size_t)nb);
+      int64_t ne = m_exact < nb ? m_exact : nb;
+      for (int64_t i = 0; i < ne; ++i) exact[tm[i].v] = 1;
+      /* step 10: inclusion probabilities of the residual (tm[ne..nb) is the
+       * residual in descending mass) */
+      int64_t nr = nb - ne;
+      for (int64_t v = 0; v < nb; ++v) pi[v] = exact[v] ? 1.0 : 0.0;
+      if (nr <= m_sample) {
+        for (int64_t i = ne; i < nb; ++i) pi[tm[i].v] = 1.0;
+      } else {
+        /* suffix sums of the residual masses, from the smallest up */
+        double *suf = a; /* reuse: a is no longer needed */
+        double run = 0.0;
+        for (int64_t i = nb - 1; i >= ne; --i) {
+          run += tm[i].mass;
+          suf[i] = run;
+        }
+        /* the number k of capped tiles: the smallest k for which the k-th
+         * largest residual mass is not capped by lam_k = (m - k) / suf */
+        int64_t k = 0;
+        while (k < m_sample && (double)(m_sample - k) * tm[ne + k].mass > suf[ne + k]) ++k;
+        double lam = (double)(m_sample - k) / suf[ne + k];
+        for (int64_t i = 0; i < nr; ++i) pi[tm[ne + i].v] = i < k ? 1.0 : lam * tm[ne + i].mass;
+      }
+      /* step 11: systematic PPS over the residual in ascending v */
+      memset(keep, 0, (size_t)nb);
+      double c = 0.0, u = uoff[bh * G + g];
+      for (int64_t v = 0; v < nb; ++v) {
+        if (exact[v]) {
+          keep[v] = 1;
+          continue;
+        }
+        double lo = c;
+        c += pi[v];
+        double klo = ceil(lo - u), khi = ceil(c - u);
+        if (klo > m_sample) klo = m_sample;
+        if (khi > m_sample) khi = m_sample;
+        if (khi > klo) keep[v] = 1;
+      }
+      /* step 13: weights; rows of the group */
+      for (int64_t uq = u0; uq < u1; ++uq) {
+        int64_t r = bh * nb + uq;
+        for (int64_t v = 0; v < nb; ++v) {
+          if (!keep[v]) continue;
+          mask[r * nb + v] = 1;
+          lw_map[r * nb + v] = (!exact[v] && pi[v] < 1.0 && v != uq) ? (float)(-log(pi[v])) : 0.0f;
+        }
+      }
+      if (pi_out)
+        for (int64_t v = 0; v < nb; ++v) pi_out[(bh * G + g) * nb + v] = pi[v];
+    }
+  }
+  free(a);
+  free(pi);
+  free(keep);
+  free(exact);
+  free(tm);
+  return rc;
 }
