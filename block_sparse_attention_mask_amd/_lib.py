@@ -21,7 +21,7 @@ BSA_V_DIM_MAJOR = 1
 
 # Every symbol include/bsattn.h declares.
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_crm_build", "bsa_crm_row_ptr",
-           "bsa_crm_to_csr", "bsa_perm_from_labels",
+           "bsa_crm_to_csr", "bsa_segment_offsets", "bsa_segment_means", "bsa_is_sample", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
            "bsa_attn_fwd",
            "bsa_device_cus", "bsa_device_clock_khz")
@@ -77,6 +77,13 @@ def load():
         L.bsa_crm_row_ptr.argtypes = [P, I64, I32, P, ctypes.POINTER(I64), P]
         L.bsa_crm_to_csr.restype = ctypes.c_int
         L.bsa_crm_to_csr.argtypes = [P, I64, I32, P, P, I64, P]
+        L.bsa_segment_offsets.restype = ctypes.c_int
+        L.bsa_segment_offsets.argtypes = [P, I64, I64, I32, P, P]
+        L.bsa_segment_means.restype = ctypes.c_int
+        L.bsa_segment_means.argtypes = [P, I64x3, I32, I32, I64, I32, P, I32, I32, P, P]
+        L.bsa_is_sample.restype = ctypes.c_int
+        L.bsa_is_sample.argtypes = [P, P, P, P, I32, I32, I32, I32, I64, I32, I32, I32, I32, ctypes.c_float,
+                                    P, P, P, P]
         L.bsa_perm_from_labels.restype = ctypes.c_int
         L.bsa_perm_from_labels.argtypes = [P, I64, I64, I32, P, P]
         for fn in (L.bsa_permute_rows, L.bsa_unpermute_rows):

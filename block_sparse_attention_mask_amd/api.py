@@ -18,7 +18,7 @@ from ._lib import AttnArgs, I64, I64x3, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
            "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus", "crm_build",
-           "crm_row_ptr", "crm_to_csr"]
+           "crm_row_ptr", "crm_to_csr", "segment_offsets", "segment_means", "is_sample"]
 
 _BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
 
@@ -161,6 +161,68 @@ def crm_to_csr(crm: torch.Tensor, nKB: int, row_ptr: torch.Tensor, nnz: int, col
     check("bsa_crm_to_csr", load().bsa_crm_to_csr(_ptr(crm), R, nKB, _ptr(row_ptr), _ptr(col), col.numel(),
                                                   _stream(stream)))
     return col[:nnz]
+
+
+def segment_offsets(labels: torch.Tensor, G: int, seg_ptr: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """bsa_segment_offsets -> int32 [BH][G+1]."""
+    _dev(labels, "labels", torch.int32)
+    if labels.dim() != 2 or not labels.is_contiguous():
+        raise ValueError("labels must be contiguous [BH][N]")
+    BH, N = labels.shape
+    if seg_ptr is None:
+        seg_ptr = torch.empty((BH, G + 1), dtype=torch.int32, device=labels.device)
+    check("bsa_segment_offsets", load().bsa_segment_offsets(_ptr(labels), BH, N, int(G), _ptr(seg_ptr),
+                                                            _stream(stream)))
+    return seg_ptr
+
+
+def segment_means(x: torch.Tensor, seg_ptr: Optional[torch.Tensor] = None, seg_len: int = 0,
+                  means: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bsa_segment_means -> float32 [B*H][G][d]; segments from seg_ptr [B*H][G+1]
+    or of fixed length seg_len."""
+    _dev(x, "x", _BF16_LIKE)
+    B, H, N, d = x.shape
+    if seg_ptr is not None:
+        _dev(seg_ptr, "seg_ptr", torch.int32)
+        if seg_ptr.shape != (B * H, seg_ptr.shape[1]) or not seg_ptr.is_contiguous():
+            raise ValueError("seg_ptr must be contiguous [B*H][G+1]")
+        G = seg_ptr.shape[1] - 1
+    else:
+        G = -(-N // seg_len)
+    if means is None:
+        means = torch.empty((B * H, G, d), dtype=torch.float32, device=x.device)
+    check("bsa_segment_means", load().bsa_segment_means(_ptr(x), _strides(x), B, H, N, d, _ptr(seg_ptr), int(G),
+                                                        int(seg_len), _ptr(means), _stream(stream)))
+    return means
+
+
+def is_sample(qbar: torch.Tensor, kbar: torch.Tensor, q_seg_ptr: torch.Tensor, uoff: torch.Tensor, B: int, Hq: int,
+              Hkv: int, N: int, block: int, m_exact: int, m_sample: int, scale: float = 0.0, want_pi: bool = False,
+              mask=None, lw_map=None, stream=None):
+    """bsa_is_sample -> (mask uint8 [B*Hq*nKB][nKB], lw_map float32, pi float64 [B*Hq][G][nKB] or None)."""
+    _dev(qbar, "qbar", torch.float32)
+    _dev(kbar, "kbar", torch.float32)
+    _dev(q_seg_ptr, "q_seg_ptr", torch.int32)
+    _dev(uoff, "uoff", torch.float64)
+    G, d = qbar.shape[1], qbar.shape[2]
+    nb = -(-N // block)
+    if (qbar.shape != (B * Hq, G, d) or kbar.shape != (B * Hkv, nb, d) or q_seg_ptr.shape != (B * Hq, G + 1)
+            or uoff.shape != (B * Hq, G)):
+        raise ValueError("qbar [B*Hq][G][d], kbar [B*Hkv][nKB][d], q_seg_ptr [B*Hq][G+1], uoff [B*Hq][G]")
+    for t in (qbar, kbar, q_seg_ptr, uoff):
+        if not t.is_contiguous():
+            raise ValueError("sampler inputs must be contiguous")
+    dev = qbar.device
+    if mask is None:
+        mask = torch.empty((B * Hq * nb, nb), dtype=torch.uint8, device=dev)
+    if lw_map is None:
+        lw_map = torch.empty((B * Hq * nb, nb), dtype=torch.float32, device=dev)
+    pi = torch.empty((B * Hq, G, nb), dtype=torch.float64, device=dev) if want_pi else None
+    check("bsa_is_sample", load().bsa_is_sample(_ptr(qbar), _ptr(kbar), _ptr(q_seg_ptr), _ptr(uoff), B, Hq, Hkv,
+                                                int(G), N, int(block), d, int(m_exact), int(m_sample), float(scale),
+                                                _ptr(mask), _ptr(lw_map), _ptr(pi), _stream(stream)))
+    return mask, lw_map, pi
 
 
 def perm_from_labels(labels: torch.Tensor, n_clusters: int, perm=None, stream=None) -> torch.Tensor:

@@ -1,7 +1,9 @@
 """One pass of the whole block-sparse attention path on device tensors:
 
 mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill), or CRM rows
-   (bsa_crm_build) with row offsets from their popcounts (bsa_crm_row_ptr)
+   (bsa_crm_build) with row offsets from their popcounts (bsa_crm_row_ptr);
+   or, with a sampler, the mask and log-weights drawn on the device
+   (bsa_segment_offsets, bsa_segment_means, bsa_is_sample) before the CSR
 -> [cluster labels -> permutations; gather Q, K]        (permuted workloads)
 -> V gathered (when permuted) and written dim-major (bsa_transpose_rows)
 -> row schedule (bsa_schedule)
@@ -74,14 +76,22 @@ class StepResult:
 
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
-            v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False) -> StepResult:
+            v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False,
+            sampler: Optional[dict] = None) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  With
     ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
     each head's query blocks (that many subspace iterations).  With ``crm``
     the lists are CRM rows (no log-weights, dim-major V); their sizes are
-    known up front, so this path makes no host synchronisation."""
+    known up front, so this path makes no host synchronisation.  With
+    ``sampler`` = {"m_exact": E, "m_sample": S, "uoff": float64 [B*Hq][G]}
+    (a permuted workload) the block mask and log-weights come from the
+    group-shared importance sampler over the permuted Q and K instead of
+    the workload's mask."""
     crm_rows = None
+    if sampler is not None:
+        return _forward_sampled(dw, sampler, schedule, n_xcd, wave_rows, fuse_scatter, want_lse, attn_events,
+                                stream)
     if crm:
         if dw.lw_map is not None or not v_dim_major:
             raise ValueError("CRM lists carry no log-weights and need dim-major V")
@@ -130,3 +140,41 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
     return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows)
+
+
+def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: int, wave_rows: int,
+                     fuse_scatter: bool, want_lse: bool, attn_events, stream) -> StepResult:
+    """labels -> perms; Q/K gathered, V gathered and transposed; query-group
+    and tile centroids; importance-sampled mask and log-weights -> CSR;
+    schedule; attention with fused scatter-back."""
+    if not dw.permuted:
+        raise ValueError("the sampler needs cluster labels")
+    perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=stream)
+    perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=stream)
+    q = api.permute_rows(dw.q, perm_q, stream=stream)
+    k = api.permute_rows(dw.k, perm_k, stream=stream)
+    v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=stream)
+    q_seg = api.segment_offsets(dw.labels_q, dw.n_clusters, stream=stream)
+    qbar = api.segment_means(q, q_seg, stream=stream)
+    kbar = api.segment_means(k, seg_len=dw.block, stream=stream)
+    mask, lw_map, _ = api.is_sample(qbar, kbar, q_seg, sampler["uoff"], dw.B, dw.Hq, dw.Hkv, dw.N, dw.block,
+                                    sampler["m_exact"], sampler["m_sample"], stream=stream)
+    row_ptr, col, lw = api.build_csr(mask, None, 0.0, lw_map, dw.nQB, True, stream=stream)
+    order = None
+    if schedule:
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream)
+    sperm = perm_q if fuse_scatter else None
+    s = stream if stream is not None else torch.cuda.current_stream()
+    if attn_events is not None:
+        attn_events[0].record(s)
+    out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
+                            want_lse=want_lse, causal=dw.causal, v_dim_major=True, stream=stream)
+    if attn_events is not None:
+        attn_events[1].record(s)
+    if not fuse_scatter:
+        out = api.unpermute_rows(out, perm_q, stream=stream)
+        if lse is not None:
+            inv = torch.empty_like(lse)
+            inv.scatter_(1, perm_q.long(), lse)
+            lse = inv
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)

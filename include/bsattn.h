@@ -203,6 +203,83 @@ int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, i
                        int32_t iters, int32_t *perm, double *angle, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Segment offsets of labelled tokens (centroid groups).
+ *
+ * Source: InstaGen, Algorithm 1 step 1 and section 4 (queries and keys are
+ * grouped by cluster label and permuted into contiguous blocks); the tokens
+ * of label g occupy one segment of the label-sorted sequence (the order
+ * bsa_perm_from_labels produces).
+ *
+ * labels: device int32 [BH][N].  seg_ptr: device int32 [BH][G + 1] (output):
+ * seg_ptr[bh][g] = number of tokens of head bh with a label in [0, g); labels
+ * outside [0, G) are not counted (they sort after every valid label).
+ * BSA_ERR_ARG for NULL pointers, negative sizes or G <= 0;
+ * BSA_ERR_UNSUPPORTED for G > 8192 or N >= 2^31.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_segment_offsets(const int32_t *labels, int64_t BH, int64_t N, int32_t G, int32_t *seg_ptr,
+                        bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Segment means (centroids).
+ *
+ * Source: InstaGen, Algorithm 1 step 2 (the centroid of a query group and of
+ * a key cluster); at tile granularity the key cluster of a KV tile is the
+ * tile itself, with its mean key as centroid.
+ *
+ * x: bf16 [B][H][N][d] (device, element strides x_str: batch, head, token;
+ * d contiguous; 16-byte aligned base, strides multiples of 8).  Segment s of
+ * head bh = b*H + h is rows [seg_ptr[bh][s], seg_ptr[bh][s+1]) when seg_ptr
+ * != NULL (device int32 [BH][G + 1], e.g. from bsa_segment_offsets over the
+ * label-sorted rows), else rows [s*seg_len, min(N, (s+1)*seg_len)) with
+ * G = ceil(N / seg_len) segments.  means: device float32 [BH][G][d]
+ * (output): the fp32 mean of the segment's rows, 0 for an empty segment.
+ * BSA_ERR_ARG for NULL pointers, non-positive sizes, misaligned strides;
+ * BSA_ERR_UNSUPPORTED for d % 8 != 0, d > 256, a misaligned x or
+ * B*H > 65535.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_segment_means(const void *x, const int64_t x_str[3], int32_t B, int32_t H, int64_t N, int32_t d,
+                      const int32_t *seg_ptr, int32_t G, int32_t seg_len, float *means, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Group-shared importance sampling over KV tiles.
+ *
+ * Source: InstaGen, Algorithm 1 steps 2-13, section 3.2.1 Eq. (4) and the
+ * systematic PPS sample of section 4, at tile granularity (each 128-key tile
+ * is entirely exact or entirely sampled; weights enter as a logit bias).
+ *
+ * For every head bh = b*Hq + h and query group g (the query blocks u whose
+ * first token u*block lies in segment g of q_seg_ptr):
+ *   - a_v = scale * qbar[bh][g] . kbar[b*Hkv + h/(Hq/Hkv)][v] (fp64), and
+ *     the tile mass |v| exp(a_v - max a), |v| = real keys of tile v;
+ *   - exact set: the m_exact tiles of largest mass (ties to the lower v);
+ *   - residual: pi_v = min(1, lam * mass_v) with sum m_sample (Eq. 4), or 1
+ *     for every residual tile when there are at most m_sample;
+ *   - sample: systematic PPS over the residual in ascending v with the points
+ *     uoff[bh][g] + j, j = 0..m_sample-1 (uoff in [0, 1), drawn by the
+ *     caller);
+ *   - rows: mask[r][v] = 1 for exact and sampled tiles, lw_map[r][v] =
+ *     -ln(pi_v) for sampled tiles with pi_v < 1, else 0 (0 on the diagonal
+ *     v = u, which the CSR builder forces as exact).
+ * Rows r = bh*nKB + u with no group are written as zeros; every row is
+ * written.  The outputs feed bsa_csr_count / bsa_csr_fill (mask, lw_map,
+ * force_diag = 1).
+ *
+ * qbar: device float32 [B*Hq][G][d]; kbar: device float32 [B*Hkv][nKB][d]
+ * (nKB = ceil(N / block)); q_seg_ptr: device int32 [B*Hq][G + 1]; uoff:
+ * device float64 [B*Hq][G]; mask: device uint8 [B*Hq*nKB][nKB]; lw_map:
+ * device float32, same shape; pi_out: optional device float64
+ * [B*Hq][G][nKB] (pi of every tile, 1 for exact tiles; 0 for groups without
+ * a query block).  scale <= 0 selects 1/sqrt(d).  BSA_ERR_ARG for NULL
+ * pointers, non-positive sizes, Hq % Hkv != 0 or negative budgets;
+ * BSA_ERR_UNSUPPORTED for nKB > 1024, d > 256, G > 65535 or B*Hq > 65535.
+ * Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_ptr, const double *uoff, int32_t B,
+                  int32_t Hq, int32_t Hkv, int32_t G, int64_t N, int32_t block, int32_t d, int32_t m_exact,
+                  int32_t m_sample, float scale, uint8_t *mask, float *lw_map, double *pi_out,
+                  bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Row schedule (launch order of the attention kernel).
  *
  * Source: WaveAlign, section IV-D (rows in consecutive buckets of at most W,

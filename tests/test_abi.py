@@ -115,6 +115,30 @@ def test_crm_argument_errors(L):
     assert L.bsa_crm_to_csr(FAKE, 4, 0, FAKE, FAKE, 3, None) == _lib.BSA_ERR_ARG
 
 
+def test_sampler_argument_errors(L):
+    st = _lib.I64x3(1024, 128, 8)
+    assert L.bsa_segment_offsets(None, 2, 10, 4, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_segment_offsets(FAKE, 2, 10, 0, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_segment_offsets(FAKE, 2, 10, 9000, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_segment_means(FAKE, st, 1, 1, 10, 8, None, 0, 0, FAKE, None) == _lib.BSA_ERR_ARG       # no seg_len
+    assert L.bsa_segment_means(FAKE, st, 1, 1, 10, 12, None, 0, 4, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_segment_means(FAKE, _lib.I64x3(1024, 128, 4), 1, 1, 10, 8, None, 0, 4, FAKE, None) == \
+        _lib.BSA_ERR_ARG
+    assert L.bsa_segment_means(ctypes.c_void_p(4100), st, 1, 1, 10, 8, None, 0, 4, FAKE, None) == \
+        _lib.BSA_ERR_UNSUPPORTED
+    args = [FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 8, 1000, 64, 128, 2, 3, 0.0, FAKE, FAKE, None, None]
+    bad = list(args); bad[0] = None
+    assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_ARG
+    bad = list(args); bad[5] = 3                   # Hq % Hkv
+    assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_ARG
+    bad = list(args); bad[12] = -1                 # m_sample < 0
+    assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_ARG
+    bad = list(args); bad[8] = 64 * 1025           # more than 1024 tiles
+    assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_UNSUPPORTED
+    bad = list(args); bad[10] = 512                # d > 256
+    assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_UNSUPPORTED
+
+
 def _args(**kw):
     a = _lib.AttnArgs()
     a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
