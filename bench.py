@@ -119,6 +119,10 @@ def main():
                "mask_to_crm_ms": crm_stage_ms(dw, torch),
                "list_bytes_per_row": {"crm": 4 * W, "csr": round(4.0 + 4.0 * nnz / w.R, 1)}}
 
+    # the device importance sampler (8 exact + 8 sampled tiles per query
+    # group) on the same permuted Q and K, and attention on its lists
+    sampled = sampler_stage(dw, torch) if dw.permuted else None
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.int16, device=dev)
@@ -164,6 +168,7 @@ def main():
         "device": device_info(torch),
         "stages_ms": stages,
         "crm_lists": crm,
+        "importance_sampler": sampled,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config),
@@ -257,6 +262,62 @@ def crm_stage_ms(dw, torch):
         if i >= 2:
             ms.append(a.elapsed_time(b))
     return round(float(np.median(ms)), 4)
+
+
+def sampler_stage(dw, torch, m_exact=8, m_sample=8):
+    """Median of 10 (after 2 warm-up passes) of each step of the sampled
+    mask: query-group offsets, query-group and tile centroids, the sampler,
+    the CSR build; then the attention launch on the sampled lists."""
+    from block_sparse_attention_mask_amd import api
+    s = torch.cuda.current_stream()
+    pq = api.perm_from_labels(dw.labels_q, dw.n_clusters)
+    pk = api.perm_from_labels(dw.labels_k, dw.n_clusters)
+    q = api.permute_rows(dw.q, pq)
+    k = api.permute_rows(dw.k, pk)
+    v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
+    gen = torch.Generator(device="cpu").manual_seed(4321)
+    uoff = torch.rand((dw.B * dw.Hq, dw.n_clusters), generator=gen, dtype=torch.float64).to(q.device)
+    names = ["segment_offsets", "query_centroids", "tile_centroids", "is_sample", "mask_to_csr"]
+    times = {n: [] for n in names}
+    res = None
+    for it in range(12):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(s)
+        seg = api.segment_offsets(dw.labels_q, dw.n_clusters)
+        ev[1].record(s)
+        qbar = api.segment_means(q, seg)
+        ev[2].record(s)
+        kbar = api.segment_means(k, seg_len=dw.block)
+        ev[3].record(s)
+        mask, lw_map, _ = api.is_sample(qbar, kbar, seg, uoff, dw.B, dw.Hq, dw.Hkv, dw.N, dw.block, m_exact,
+                                        m_sample)
+        ev[4].record(s)
+        res = api.build_csr(mask, None, 0.0, lw_map, dw.nQB, True)
+        ev[5].record(s)
+        torch.cuda.synchronize()
+        if it >= 2:
+            for i, n in enumerate(names):
+                times[n].append(ev[i].elapsed_time(ev[i + 1]))
+    row_ptr, col, lw = res
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, 0, 8)
+    ms = []
+    for it in range(12):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq, v_dim_major=True)
+        b.record(s)
+        torch.cuda.synchronize()
+        if it >= 2:
+            ms.append(a.elapsed_time(b))
+    from block_sparse_attention_mask_amd import metrics
+    nnz = int(row_ptr[-1].item())
+    pairs = metrics.count_pairs(row_ptr.cpu().numpy(), col[:nnz].cpu().numpy(), dw.N, dw.block, dw.causal)
+    att = float(np.median(ms))
+    out = {n: round(float(np.median(t)), 4) for n, t in times.items()}
+    out.update({"budget_tiles": {"exact": m_exact, "sampled": m_sample}, "nnz_blocks": nnz,
+                "attention_ms": round(att, 4),
+                "attention_tflops": round(4.0 * dw.d * pairs / (att * 1e-3) / 1e12, 2)})
+    return out
 
 
 def device_info(torch):
