@@ -420,6 +420,80 @@ def random_case(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, block: int
     return w
 
 
+# --------------------------------------------------------------------------
+# Token-level computational query sets: index maps only
+# --------------------------------------------------------------------------
+def _lists_to_csr(qsets, ksets, BQ):
+    C = len(qsets)
+    q_idx = np.full((C, BQ), -1, dtype=np.int32)
+    for i, qs in enumerate(qsets):
+        q_idx[i, :len(qs)] = qs
+    kv_ptr = np.zeros(C + 1, dtype=np.int32)
+    kv_ptr[1:] = np.cumsum([len(k) for k in ksets])
+    kv_idx = np.concatenate(ksets).astype(np.int32) if C else np.zeros(0, np.int32)
+    return q_idx, kv_ptr, kv_idx
+
+
+def cqs_scatter(N: int, R: int = 8, BQ: int = 64, causal: bool = False):
+    """INTRA Scatter (sections 4.2 and 4.8): relay group r holds the tokens
+    r, r + R, r + 2R, ... (one token of every R-token neighbourhood); each
+    query set is BQ consecutive members of one group and its keys are the
+    group's members (when causal, only those up to the set's last query).
+    Returns (q_idx [C][BQ], kv_ptr [C+1], kv_idx) for one head."""
+    qsets, ksets = [], []
+    for r in range(R):
+        members = np.arange(r, N, R)
+        for b0 in range(0, len(members), BQ):
+            qsets.append(members[b0:b0 + BQ])
+            ksets.append(members[:b0 + BQ] if causal else members)
+    return _lists_to_csr(qsets, ksets, BQ)
+
+
+def cqs_gather0(H: int, W: int):
+    """INTRA Gather 0 (appendix, sparse pattern index functions): query set i
+    is the 8x8 patch (r, c) = divmod(i, W / 8) of an H x W token image
+    (row-major); its keys are the 16 x 16 window with top-left corner
+    (clamp(8r - 4, 0, H - 16), clamp(8c - 4, 0, W - 16)), taken as four
+    64-key tiles of four rows of 16 keys.  Returns (q_idx [C][64], kv_ptr
+    [C+1], kv_idx) for one head."""
+    assert H >= 16 and W >= 16 and H % 8 == 0 and W % 8 == 0
+    qsets, ksets = [], []
+    for i in range((H // 8) * (W // 8)):
+        r, c = divmod(i, W // 8)
+        il = np.arange(64)
+        qsets.append((8 * r + il // 8) * W + 8 * c + il % 8)
+        r0 = min(max(8 * r - 4, 0), H - 16)
+        c0 = min(max(8 * c - 4, 0), W - 16)
+        jl = np.arange(256)
+        ksets.append((r0 + jl // 16) * W + c0 + jl % 16)
+    return _lists_to_csr(qsets, ksets, 64)
+
+
+def cqs_token_select(seed: int, N: int, BQ: int, n_keys: int):
+    """Token-level KV selection shape (MC-Sparse): the sequence (in its
+    grouped order) splits into query groups of BQ consecutive tokens, and each
+    group attends to its own n_keys distinct key tokens, drawn uniformly
+    without replacement and listed in ascending order.  Returns (q_idx
+    [C][BQ], kv_ptr [C+1], kv_idx) for one head."""
+    g = _streams(seed, 1)[0]
+    qsets, ksets = [], []
+    for b0 in range(0, N, BQ):
+        qsets.append(np.arange(b0, min(N, b0 + BQ)))
+        ksets.append(np.sort(g.choice(N, size=min(n_keys, N), replace=False)))
+    return _lists_to_csr(qsets, ksets, BQ)
+
+
+def cqs_per_head(maps, BH: int):
+    """Stacks one head's (q_idx, kv_ptr, kv_idx) for BH heads (the same sets
+    in every head)."""
+    q_idx, kv_ptr, kv_idx = maps
+    C = q_idx.shape[0]
+    nnz = int(kv_ptr[-1])
+    ptr = (kv_ptr[None, :-1].astype(np.int64) + nnz * np.arange(BH)[:, None]).reshape(-1)
+    kv_ptr_all = np.concatenate([ptr, [nnz * BH]]).astype(np.int32)
+    return (np.broadcast_to(q_idx, (BH, C, q_idx.shape[1])).copy(), kv_ptr_all, np.tile(kv_idx, BH))
+
+
 CONFIGS = {
     "tiny": tiny,
     "video_threshold": video_threshold,

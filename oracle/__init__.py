@@ -53,6 +53,9 @@ def lib():
         L.oracle_is_sample.restype = ctypes.c_int
         L.oracle_is_sample.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int32, I64, ctypes.c_int32, I64,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P, P]
+        L.oracle_attn_tok.restype = ctypes.c_int
+        L.oracle_attn_tok.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, P, P, P, ctypes.c_int,
+                                      ctypes.c_double, I64, P, P, P]
         L.oracle_perm_from_labels.restype = ctypes.c_int
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
@@ -246,6 +249,39 @@ def attn_rows(q, k, v, row_ptr, col, lw, block: int, rows: np.ndarray, perm_q=No
                                 float(scale), len(rows), _p(rows), _p(out), _p(lse))
     if rc:
         raise ValueError("oracle_attn_rows failed: %d" % rc)
+    return out, lse
+
+
+def attn_tok(q, k, v, q_idx, kv_ptr, kv_idx, slots=None, causal: bool = False, scale: Optional[float] = None):
+    """Token-level attention over computational query sets.  q [B][Hq][N][d],
+    k/v [B][Hkv][N][d] uint16 bf16 bits; q_idx int32 [B*Hq][C][BQ]; kv_ptr
+    int32 [B*Hq*C + 1]; kv_idx int32.  slots: flat (bh*C + c)*BQ + i (all by
+    default).  Returns (O float64 [n][d], LSE float64 [n]; NaN for empty
+    slots)."""
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    for a in (q, k, v):
+        assert a.dtype == np.uint16 and a.strides[-1] == 2
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    q_idx = np.ascontiguousarray(q_idx, dtype=np.int32)
+    C, BQ = q_idx.shape[1], q_idx.shape[2]
+    kv_ptr = np.ascontiguousarray(kv_ptr, dtype=np.int32)
+    kv_idx = np.ascontiguousarray(kv_idx, dtype=np.int32)
+    if kv_idx.size == 0:
+        kv_idx = np.zeros(1, np.int32)
+    if slots is None:
+        slots = np.arange(B * Hq * C * BQ, dtype=np.int64)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    st = lambda a: np.array([s // 2 for s in a.strides[:3]], dtype=np.int64)
+    out = np.empty((len(slots), d), dtype=np.float64)
+    lse = np.empty(len(slots), dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rc = lib().oracle_attn_tok(_p(q), _p(k), _p(v), _p(st(q)), _p(st(k)), _p(st(v)), B, Hq, Hkv, N, d, C, BQ,
+                               _p(q_idx), _p(kv_ptr), _p(kv_idx), int(causal), float(scale), len(slots), _p(slots),
+                               _p(out), _p(lse))
+    if rc:
+        raise ValueError("oracle_attn_tok failed: %d" % rc)
     return out, lse
 
 

@@ -62,6 +62,14 @@
  *                     Eq. 4): centroid scores, the exact set by decreasing
  *                     size x score, water-filled inclusion probabilities,
  *                     a systematic PPS sample, Horvitz-Thompson log-weights.
+ *  oracle_attn_tok    Token-level attention over computational query sets
+ *                     (INTRA, sections 3 and 4.8: a CQS is a group of query
+ *                     tokens given by a query mapping, attending to the key
+ *                     tokens given by a key mapping; outputs go back to the
+ *                     query positions).  InstaGen Eq. (1)-(3) over the
+ *                     CQS's key list, one term per list entry; entries
+ *                     outside the sequence and, when causal, keys after the
+ *                     query are left out.
  *  oracle_count_pairs Number of allowed (query, key) token pairs; the FLOP
  *                     convention of 4*d per pair is the one behind INTRA's
  *                     GFLOPS column (INTRA, Table 1 and the overhead table).
@@ -711,4 +719,80 @@ int oracle_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_
   free(exact);
   free(tm);
   return rc;
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* token-level attention over computational query sets                      */
+/* ------------------------------------------------------------------------ */
+/* CQS c of head bh = b*Hq + h: query positions q_idx[(bh*C + c)*BQ + i]
+ * (i < BQ; a position outside [0, N) is an empty slot) and key positions
+ * kv_idx[kv_ptr[bh*C + c] .. kv_ptr[bh*C + c + 1]).  For each requested slot
+ * (slots[j] = (bh*C + c)*BQ + i): O = sum_e softmax_e(x_e) V[s_e] over the
+ * list entries e with s_e in [0, N) and, when causal, s_e <= t, with
+ * x_e = scale * Q[t] . K[s_e] (K and V of head b*Hkv + h/(Hq/Hkv));
+ * LSE = ln sum_e exp(x_e).  No allowed entry: O = 0, LSE = -inf.  An empty
+ * slot gives O = 0 and LSE = NaN. */
+int oracle_attn_tok(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *q_str,
+                    const int64_t *k_str, const int64_t *v_str, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                    int64_t d, int64_t C, int64_t BQ, const int32_t *q_idx, const int32_t *kv_ptr,
+                    const int32_t *kv_idx, int causal, double scale, int64_t n_slots, const int64_t *slots,
+                    double *out, double *lse) {
+  if (!q || !k || !v || !q_idx || !kv_ptr || !kv_idx || !slots || !out || !lse) return OR_ERR_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N <= 0 || d <= 0 || C <= 0 || BQ <= 0) return OR_ERR_ARG;
+  int64_t G = Hq / Hkv;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t j = 0; j < n_slots; ++j) {
+      int64_t slot = slots[j];
+      int64_t cq = slot / BQ;
+      if (slot < 0 || cq >= B * Hq * C) {
+        bad = 1;
+        continue;
+      }
+      int64_t bh = cq / C, b = bh / Hq, h = bh % Hq, g = h / G;
+      int64_t t = q_idx[slot];
+      for (int64_t c = 0; c < d; ++c) out[j * d + c] = 0.0;
+      if (t < 0 || t >= N) {
+        lse[j] = NAN;
+        continue;
+      }
+      const uint16_t *qrow = q + b * q_str[0] + h * q_str[1] + t * q_str[2];
+      for (int64_t c = 0; c < d; ++c) qv[c] = bf16_to_double(qrow[c]);
+      int32_t e0 = kv_ptr[cq], e1 = kv_ptr[cq + 1];
+      double m = -INFINITY;
+      for (int32_t e = e0; e < e1; ++e) {
+        int64_t s = kv_idx[e];
+        if (s < 0 || s >= N || (causal && s > t)) continue;
+        const uint16_t *krow = k + b * k_str[0] + g * k_str[1] + s * k_str[2];
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qv[c] * bf16_to_double(krow[c]);
+        if (scale * dot > m) m = scale * dot;
+      }
+      double Z = 0.0;
+      for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+      if (m != -INFINITY) {
+        for (int32_t e = e0; e < e1; ++e) {
+          int64_t s = kv_idx[e];
+          if (s < 0 || s >= N || (causal && s > t)) continue;
+          const uint16_t *krow = k + b * k_str[0] + g * k_str[1] + s * k_str[2];
+          double dot = 0.0;
+          for (int64_t c = 0; c < d; ++c) dot += qv[c] * bf16_to_double(krow[c]);
+          double w = exp(scale * dot - m);
+          Z += w;
+          const uint16_t *vrow = v + b * v_str[0] + g * v_str[1] + s * v_str[2];
+          for (int64_t c = 0; c < d; ++c) acc[c] += w * bf16_to_double(vrow[c]);
+        }
+      }
+      for (int64_t c = 0; c < d; ++c) out[j * d + c] = Z > 0.0 ? acc[c] / Z : 0.0;
+      lse[j] = Z > 0.0 ? m + log(Z) : -INFINITY;
+    }
+    free(qv);
+    free(acc);
+  }
+  return bad ? OR_ERR_ARG : OR_OK;
 }
