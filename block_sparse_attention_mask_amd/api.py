@@ -14,11 +14,12 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import AttnArgs, I64, I64x3, check, load
+from ._lib import AttnArgs, I64, I64x3, TokArgs, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
            "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus", "crm_build",
-           "crm_row_ptr", "crm_to_csr", "segment_offsets", "segment_means", "is_sample"]
+           "crm_row_ptr", "crm_to_csr", "segment_offsets", "segment_means", "is_sample",
+           "attn_tok_fwd"]
 
 _BF16_LIKE = (torch.bfloat16, torch.uint16, torch.int16)
 
@@ -341,4 +342,41 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
             raise ValueError("crm must hold B * Hq * ceil(N / block) rows")
     a.crm = _ptr(crm)
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def attn_tok_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, kv_ptr: torch.Tensor,
+                 kv_idx: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 want_lse: bool = False, scale: float = 0.0, causal: bool = False, stream=None):
+    """Token-level attention over computational query sets: q_idx int32
+    [B*Hq][n_sets][set_size] query positions, kv_ptr int32 [B*Hq*n_sets + 1]
+    and kv_idx int32 key positions; q, k, v token-major.  Returns (out, lse).
+    Rows of out at positions no set lists are left as they were (out is
+    zero-filled when allocated here)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, _BF16_LIKE)
+    for t, n in ((q_idx, "q_idx"), (kv_ptr, "kv_ptr"), (kv_idx, "kv_idx")):
+        _dev(t, n, torch.int32)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if q_idx.dim() != 3 or q_idx.shape[0] != B * Hq:
+        raise ValueError("q_idx must be [B*Hq][n_sets][set_size]")
+    n_sets, set_size = q_idx.shape[1], q_idx.shape[2]
+    if kv_ptr.numel() != B * Hq * n_sets + 1:
+        raise ValueError("kv_ptr must have B*Hq*n_sets + 1 entries")
+    if out is None:
+        out = torch.zeros((B, Hq, N, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.full((B * Hq, N), float("nan"), dtype=torch.float32, device=q.device)
+    a = TokArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.B, a.Hq, a.Hkv, a.d, a.N = B, Hq, Hkv, d, N
+    a.q_str, a.k_str, a.v_str, a.o_str = _strides(q), _strides(k), _strides(v), _strides(out)
+    a.n_sets, a.set_size = n_sets, set_size
+    a.q_idx, a.kv_ptr, a.kv_idx = _ptr(q_idx), _ptr(kv_ptr), _ptr(kv_idx)
+    a.scale = float(scale)
+    a.causal = int(bool(causal))
+    check("bsa_attn_tok_fwd", load().bsa_attn_tok_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse

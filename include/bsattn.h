@@ -358,6 +358,52 @@ typedef struct {
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Token-level attention over computational query sets.
+ *
+ * Source: INTRA, section 3 (a computational query set, CQS, is a group of
+ * query tokens evaluated together, with structured mappings to the key
+ * tokens it attends to) and section 4.8 (the selected Q, K and V tokens are
+ * loaded and packed into dense on-chip tiles, outputs are scattered back to
+ * the query positions, full or causal masking); MC-Sparse's token-level KV
+ * selection per query group is the same computation.  For every query t of
+ * set c: o_t = sum_e softmax_e(l_e) v_{s_e}, l_e = q_t . k_{s_e} * scale,
+ * over the entries e of the set's key list (InstaGen, section 3.1
+ * Eq. (1)-(3); one term per entry); entries outside [0, N) and, when causal,
+ * keys s_e > t do not take part.  A query with no entry left gets O = 0 and
+ * LSE = -inf.
+ *
+ * q [B][Hq][N][d], k and v [B][Hkv][N][d], o [B][Hq][N][d]: bf16 (uint16
+ * bits) token-major device tensors addressed by the strides (d contiguous,
+ * 16-byte aligned bases, strides multiples of 8; per-head byte extents
+ * below 2^30); query head h reads KV head h / (Hq / Hkv).  n_sets sets per
+ * head of set_size (64 or 128) query slots: q_idx (device int32
+ * [B*Hq][n_sets][set_size]) holds each slot's query position, a position
+ * outside [0, N) being an empty slot (nothing computed or written).  kv_ptr
+ * (device int32 [B*Hq*n_sets + 1]) and kv_idx (device int32) list each set's
+ * key positions, in any order.  o (and lse, float32 [B*Hq][N], optional) are
+ * written at the query positions; a position should belong to at most one
+ * set of its head (otherwise which write lands is unspecified).  o must not
+ * alias q, k or v.  d must be 128 (BSA_ERR_UNSUPPORTED otherwise, and for
+ * set_size outside {64, 128} or larger extents); BSA_ERR_ARG for NULL
+ * pointers, non-positive sizes, Hq % Hkv != 0 or misaligned strides.
+ * scale <= 0 selects 1/sqrt(d).  Asynchronous.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int32_t B, Hq, Hkv, d;
+  int64_t N;
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3];
+  int32_t n_sets, set_size;
+  const int32_t *q_idx, *kv_ptr, *kv_idx;
+  float scale;
+  int32_t causal;
+} bsa_tok_args;
+
+int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream);
+
 /* Number of compute units of the current device (for wave sizing), or a
  * negative error. */
 int bsa_device_cus(void);

@@ -139,6 +139,39 @@ def test_sampler_argument_errors(L):
     assert L.bsa_is_sample(*bad) == _lib.BSA_ERR_UNSUPPORTED
 
 
+def _tok_args(**kw):
+    a = _lib.TokArgs()
+    a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
+    a.B, a.Hq, a.Hkv, a.d, a.N = 1, 4, 2, 128, 1000
+    st = _lib.I64x3(4 * 1000 * 128, 1000 * 128, 128)
+    a.q_str = a.k_str = a.v_str = a.o_str = st
+    a.n_sets, a.set_size = 4, 64
+    a.q_idx, a.kv_ptr, a.kv_idx = FAKE, FAKE, FAKE
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.BSA_ERR_ARG),
+    (dict(q_idx=None), _lib.BSA_ERR_ARG),
+    (dict(kv_ptr=None), _lib.BSA_ERR_ARG),
+    (dict(d=64), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(set_size=32), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(Hq=3), _lib.BSA_ERR_ARG),
+    (dict(N=0), _lib.BSA_ERR_ARG),
+    (dict(q=ctypes.c_void_p(4104)), _lib.BSA_ERR_ARG),
+    (dict(k_str=_lib.I64x3(4 * 1000 * 128, 1000 * 128, 130)), _lib.BSA_ERR_ARG),
+    (dict(o=FAKE), _lib.BSA_ERR_ARG),
+    (dict(N=1 << 23), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(kv_idx=None), _lib.BSA_ERR_ARG),
+])
+def test_attn_tok_argument_errors(L, kw, code):
+    a = _tok_args(**kw)
+    assert L.bsa_attn_tok_fwd(ctypes.byref(a), None) == code
+    assert L.bsa_attn_tok_fwd(None, None) == _lib.BSA_ERR_ARG
+
+
 def _args(**kw):
     a = _lib.AttnArgs()
     a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
