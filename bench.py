@@ -39,6 +39,7 @@ def parse():
                     choices=["clustered", "importance_sampled", "video_threshold", "llm_prefill", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-token-sets", action="store_true", help="skip the token-level set measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
     ap.add_argument("--n-xcd", type=int, default=8)
@@ -123,6 +124,10 @@ def main():
     # group) on the same permuted Q and K, and attention on its lists
     sampled = sampler_stage(dw, torch) if dw.permuted else None
 
+    # token-level computational query sets (INTRA Scatter / Gather 0,
+    # MC-Sparse-shaped token selection) on their own synthetic inputs
+    token_sets = None if args.no_token_sets else token_set_stage(torch)
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
         src = torch.empty(n, dtype=torch.int16, device=dev)
@@ -169,6 +174,7 @@ def main():
         "stages_ms": stages,
         "crm_lists": crm,
         "importance_sampler": sampled,
+        "token_sets": token_sets,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config),
@@ -318,6 +324,80 @@ def sampler_stage(dw, torch, m_exact=8, m_sample=8):
                 "attention_ms": round(att, 4),
                 "attention_tflops": round(4.0 * dw.d * pairs / (att * 1e-3) / 1e12, 2)})
     return out
+
+
+def token_set_stage(torch):
+    """Token-level attention over computational query sets: median of 10
+    launches after 3 warm-up calls, effective TFLOPS (4 d per allowed pair).
+    Q, K, V ~ N(0, 1) in bf16 from a seeded device generator."""
+    from block_sparse_attention_mask_amd import api, synth
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    res = {}
+
+    def qkv(Hq, Hkv, N, d=128):
+        f = lambda H: torch.randn((1, H, N, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        return f(Hq), f(Hkv), f(Hkv)
+
+    def timed(name, shape, q, k, v, q_idx, kv_ptr, kv_idx, causal, pairs):
+        out = torch.empty_like(q)
+        for _ in range(3):
+            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal)
+        s = torch.cuda.current_stream()
+        ms = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal)
+            b.record(s)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        t = float(np.median(ms))
+        tf = 4.0 * q.shape[3] * pairs / (t * 1e-3) / 1e12
+        res[name] = {"shape": shape, "ms": round(t, 4), "tflops": round(tf, 2),
+                     "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "allowed_pairs": int(pairs)}
+        log("token sets %s: %.3f ms, %.1f TFLOPS" % (name, t, tf))
+
+    # INTRA Scatter, LLaMA-3.1-8B prefill shape at 32K: 8 relay groups, causal
+    N, Hq, Hkv, R = 32768, 32, 8, 8
+    maps = synth.cqs_per_head(synth.cqs_scatter(N, R, 64, True), Hq)
+    T = N // R
+    pairs = Hq * R * T * (T + 1) // 2
+    qkv_s = qkv(Hq, Hkv, N)
+    timed("intra_scatter_llama3_8b_32k", "1x32q/8kv x 32768, d128, 8 groups, causal, 64-query sets",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
+    # the same pattern executed as 128-query sets (two consecutive 64-query
+    # sets of a group share the later one's key list; causal masking keeps
+    # the computation identical)
+    maps = synth.cqs_per_head(synth.cqs_scatter(N, R, 128, True), Hq)
+    timed("intra_scatter_llama3_8b_32k_sets128", "same, 128-query sets",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
+    del qkv_s
+    # INTRA Gather 0, FLUX.1-dev 2048x2048 image (128x128 tokens): 8x8 patches, 16x16 windows
+    H = W = 128
+    heads = 24
+    maps = synth.cqs_per_head(synth.cqs_gather0(H, W), heads)
+    timed("intra_gather0_flux_128x128", "1x24 x 16384 image tokens, d128, 8x8 query patches, 16x16 key windows",
+          *qkv(heads, heads, H * W), *(torch.from_numpy(x).to(dev) for x in maps), False, heads * H * W * 256)
+    # token-level KV selection, Wan2.1-14B shape: 128-query groups, 15 % of the keys each
+    N, heads, BQ = 75600, 40, 128
+    K = int(0.15 * N)
+    C = -(-N // BQ)
+    q_idx = torch.arange(C * BQ, device=dev, dtype=torch.int32).reshape(1, C, BQ)
+    q_idx = torch.where(q_idx < N, q_idx, torch.full_like(q_idx, -1)).expand(heads, C, BQ).contiguous()
+    parts = []
+    for h in range(heads):
+        r = torch.rand((C, N), generator=gen, device=dev)
+        parts.append(torch.topk(r, K, dim=1).indices.sort(dim=1).values.to(torch.int32).reshape(-1))
+        del r
+    kv_idx = torch.cat(parts)
+    del parts
+    kv_ptr = (torch.arange(heads * C + 1, device=dev, dtype=torch.int64) * K).to(torch.int32)
+    timed("token_select_wan14b_15pct", "1x40 x 75600, d128, 128-query groups, 11340 keys each",
+          *qkv(heads, heads, N), q_idx, kv_ptr, kv_idx, False, heads * N * K)
+    del kv_idx
+    torch.cuda.empty_cache()
+    return res
 
 
 def device_info(torch):
