@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-token-sets", action="store_true", help="skip the token-level set measurements")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip every measurement beside the headline step (CRM lists, sampler, token sets), "
+                         "so that a profile holds only the headline kernel's launches")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
     ap.add_argument("--n-xcd", type=int, default=8)
@@ -113,7 +116,7 @@ def main():
     # the same launch with CRM rows in place of the CSR lists (workloads
     # without log-weights), and the mask -> CRM stage
     crm = None
-    if dw.lw_map is None:
+    if dw.lw_map is None and not args.headline_only:
         crm_solo = attention_alone(dw, args, torch, crm=True)
         W = -(-w.nQB // 32)
         crm = {"alone_median50_ms": crm_solo["median_ms"], "l2_flushed_ms": crm_solo["flushed_ms"],
@@ -122,11 +125,11 @@ def main():
 
     # the device importance sampler (8 exact + 8 sampled tiles per query
     # group) on the same permuted Q and K, and attention on its lists
-    sampled = sampler_stage(dw, torch) if dw.permuted else None
+    sampled = sampler_stage(dw, torch) if (dw.permuted and not args.headline_only) else None
 
     # token-level computational query sets (INTRA Scatter / Gather 0,
     # MC-Sparse-shaped token selection) on their own synthetic inputs
-    token_sets = None if args.no_token_sets else token_set_stage(torch)
+    token_sets = None if (args.no_token_sets or args.headline_only) else token_set_stage(torch)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
