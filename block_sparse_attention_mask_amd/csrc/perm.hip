@@ -6,88 +6,103 @@
 // afterwards (WaveAlign, section V: permute query rows, restore outputs).
 //
 // perm_from_labels is a stable counting sort by (label, original index): one
-// workgroup per (batch, head); each of its four wavefronts owns a contiguous
-// quarter of the tokens.  Pass 1 histograms labels per quarter in LDS, a scan
-// turns the histograms into per-(quarter, label) write cursors, pass 2 walks
-// each quarter in token order 64 tokens at a time: lanes with equal labels
+// workgroup per (batch, head); each of its W wavefronts owns a contiguous
+// W-th of the tokens (W = 16 for up to 1023 clusters, else 4).  Pass 1
+// histograms labels per wavefront in LDS, a scan turns the histograms into
+// per-(wavefront, label) write cursors in label-major order, pass 2 walks
+// each wavefront's tokens in order 64 at a time: lanes with equal labels
 // find each other with one ballot per label bit, take their rank among the
-// lower lanes, and the lowest of them advances the cursor.
+// lower lanes, and the lowest of them advances the cursor.  Both passes load
+// eight 64-token groups of labels at once, so the loads overlap.
 #include "bsa_internal.h"
 
 namespace {
 
-constexpr int kPermWaves = 4;
 constexpr int kMaxClusters = 4095;  // + 1 overflow bucket for out-of-range labels
+constexpr int kBatch = 8;           // 64-token groups of labels loaded at once
 
-__global__ __launch_bounds__(256) void perm_from_labels_kernel(const int32_t *__restrict__ labels,
-                                                               int64_t N, int C,
-                                                               int32_t *__restrict__ perm) {
-  __shared__ int32_t cur[kPermWaves][kMaxClusters + 1];
-  __shared__ int32_t tot[256];
+template <int W, int MAXB>
+__global__ __launch_bounds__(64 * W) void perm_from_labels_kernel(const int32_t *__restrict__ labels, int64_t N,
+                                                                  int C, int32_t *__restrict__ perm) {
+  constexpr int NT = 64 * W;
+  __shared__ int32_t cur[W][MAXB];
+  __shared__ int32_t tot[NT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t bh = blockIdx.x;
   const int32_t *lab = labels + bh * N;
   int32_t *out = perm + bh * N;
   const int nb = C + 1;  // buckets; bucket C collects out-of-range labels
-  for (int i = tid; i < kPermWaves * nb; i += 256) cur[i / nb][i % nb] = 0;
+  for (int i = tid; i < W * nb; i += NT) cur[i / nb][i % nb] = 0;
   __syncthreads();
-  const int64_t seg = (N + kPermWaves - 1) / kPermWaves;
+  const int64_t seg = (N + W - 1) / W;
   const int64_t s0 = wave * seg;
   const int64_t s1 = s0 + seg < N ? s0 + seg : N;
-  for (int64_t t = s0 + lane; t < s1; t += 64) {
-    int32_t l = lab[t];
-    if (l < 0 || l >= C) l = C;
-    atomicAdd(&cur[wave][l], 1);
+  auto bucket = [&](int32_t l) { return (l < 0 || l >= C) ? C : l; };
+  for (int64_t t0 = s0; t0 < s1; t0 += 64 * kBatch) {
+    int32_t l[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t t = t0 + 64 * k + lane;
+      l[k] = t < s1 ? lab[t] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (t0 + 64 * k + lane < s1) atomicAdd(&cur[wave][bucket(l[k])], 1);
   }
   __syncthreads();
-  // exclusive scan in bucket-major, quarter-minor order
-  const int per = (nb + 255) / 256;
-  const int b0 = tid * per, b1 = b0 + per < nb ? b0 + per : nb;
+  // exclusive scan over entries e = bucket * W + wave (label-major)
+  const int ne = nb * W;
+  const int per = (ne + NT - 1) / NT;
+  const int e0 = tid * per, e1 = e0 + per < ne ? e0 + per : ne;
   int32_t s = 0;
-  for (int bk = b0; bk < b1; ++bk)
-    for (int w = 0; w < kPermWaves; ++w) s += cur[w][bk];
+  for (int e = e0; e < e1; ++e) s += cur[e % W][e / W];
   tot[tid] = s;
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 256; ++i) {
-      int32_t x = tot[i];
-      tot[i] = run;
-      run += x;
-    }
+  for (int off = 1; off < NT; off <<= 1) {
+    const int32_t x = tid >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += x;
+    __syncthreads();
   }
-  __syncthreads();
-  int32_t run = tot[tid];
-  for (int bk = b0; bk < b1; ++bk)
-    for (int w = 0; w < kPermWaves; ++w) {
-      int32_t x = cur[w][bk];
-      cur[w][bk] = run;
-      run += x;
-    }
+  int32_t run = tid ? tot[tid - 1] : 0;
+  for (int e = e0; e < e1; ++e) {
+    const int32_t x = cur[e % W][e / W];
+    cur[e % W][e / W] = run;
+    run += x;
+  }
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < nb) ++nbits;
   const uint64_t below = bsa_lanemask_lt(lane);
-  for (int64_t c0 = s0; c0 < s1; c0 += 64) {
-    const int64_t t = c0 + lane;
-    const bool valid = t < s1;
-    int32_t l = valid ? lab[t] : 0;
-    if (l < 0 || l >= C) l = C;
-    uint64_t same = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = (l >> bit) & 1;
-      const uint64_t bal = __ballot(set);
-      same &= set ? bal : ~bal;
+  for (int64_t t0 = s0; t0 < s1; t0 += 64 * kBatch) {
+    int32_t l[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t t = t0 + 64 * k + lane;
+      l[k] = t < s1 ? bucket(lab[t]) : 0;
     }
-    int32_t base = 0;
-    if (valid) base = cur[wave][l];
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      const int rank = __popcll(same & below);
-      out[base + rank] = (int32_t)t;
-      if (rank == 0) cur[wave][l] = base + __popcll(same);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int64_t c0 = t0 + 64 * k;
+      if (c0 >= s1) break;
+      const int64_t t = c0 + lane;
+      const bool valid = t < s1;
+      uint64_t same = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (l[k] >> bit) & 1;
+        const uint64_t bal = __ballot(set);
+        same &= set ? bal : ~bal;
+      }
+      int32_t base = 0;
+      if (valid) base = cur[wave][l[k]];
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        const int rank = __popcll(same & below);
+        out[base + rank] = (int32_t)t;
+        if (rank == 0) cur[wave][l[k]] = base + __popcll(same);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -210,8 +225,12 @@ extern "C" int bsa_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N
   if (n_clusters > kMaxClusters) return BSA_ERR_UNSUPPORTED;
   if (N >= (int64_t(1) << 31) || BH >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   if (BH == 0 || N == 0) return BSA_OK;
-  hipLaunchKernelGGL(perm_from_labels_kernel, dim3((unsigned)BH), dim3(256), 0,
-                     bsa_hip_stream(stream), labels, N, n_clusters, perm);
+  if (n_clusters + 1 <= 1024)
+    hipLaunchKernelGGL((perm_from_labels_kernel<16, 1024>), dim3((unsigned)BH), dim3(1024), 0,
+                       bsa_hip_stream(stream), labels, N, n_clusters, perm);
+  else
+    hipLaunchKernelGGL((perm_from_labels_kernel<4, kMaxClusters + 1>), dim3((unsigned)BH), dim3(256), 0,
+                       bsa_hip_stream(stream), labels, N, n_clusters, perm);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

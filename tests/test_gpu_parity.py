@@ -87,6 +87,18 @@ def test_order_invariance_and_determinism(vdm):
     assert np.array_equal(r1.lse.cpu().numpy(), r3.lse.cpu().numpy())
 
 
+@pytest.mark.parametrize("BH,N,C", [(3, 75600, 64), (2, 5000, 1023), (2, 5000, 1024), (1, 9000, 3000),
+                                    (4, 17, 5), (2, 64 * 16 * 8 + 1, 7)])
+def test_perm_from_labels_bit_exact(BH, N, C):
+    """Both kernel shapes (16 wavefronts up to 1023 clusters, 4 above), out-of-range
+    labels, segments shorter than one load batch and exactly one batch long."""
+    rng = np.random.default_rng(N + C)
+    labels = rng.integers(-2, C + 2, size=(BH, N), dtype=np.int32)
+    _log("case perm BH=%d N=%d C=%d" % (BH, N, C))
+    got = api.perm_from_labels(torch.from_numpy(labels).cuda(), C).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.perm_from_labels(labels, C))
+
+
 def test_perm_and_row_gather_bit_exact():
     rng = np.random.default_rng(77)
     labels = rng.integers(-1, 40, size=(6, 3001), dtype=np.int32)   # includes out-of-range
