@@ -40,6 +40,7 @@ class AttnArgs(ctypes.Structure):
         ("causal", I32),
         ("v_layout", I32),
         ("crm", P),
+        ("gather_perm_q", P),
     ]
 
 

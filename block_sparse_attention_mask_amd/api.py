@@ -311,11 +311,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
              order: Optional[torch.Tensor] = None, scatter_perm_q: Optional[torch.Tensor] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = False, scale: float = 0.0, causal: bool = False,
-             v_dim_major: bool = False, crm: Optional[torch.Tensor] = None, stream=None):
+             v_dim_major: bool = False, crm: Optional[torch.Tensor] = None,
+             gather_perm_q: Optional[torch.Tensor] = None, stream=None):
     """Block-sparse attention forward; returns (out, lse or None).  With
     ``v_dim_major`` v is [B][Hkv][d][ld] (keys contiguous, from transpose_rows),
     otherwise [B][Hkv][N][d].  With ``crm`` (CRM rows from crm_build) the lists
-    come from the bitmask words and row_ptr/col may be None."""
+    come from the bitmask words and row_ptr/col may be None.  With
+    ``gather_perm_q`` q is unpermuted and the kernel reads query row
+    gather_perm_q[bh][i] for permuted position i."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     B, Hq, N, d = q.shape
@@ -341,6 +344,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
         if _crm_rows(crm, nQB) != B * Hq * nQB:
             raise ValueError("crm must hold B * Hq * ceil(N / block) rows")
     a.crm = _ptr(crm)
+    a.gather_perm_q = _ptr(gather_perm_q)
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse
 

@@ -27,6 +27,7 @@ struct AttnParams {
   const float *lw;
   const int32_t *order;
   const int32_t *sperm;
+  const int32_t *gperm;  // query gather: permuted position -> row of q, or null
   int64_t N, R;
   int Hq, G, nQB, causal;
   float c;  // softmax scale * log2(e)

@@ -113,11 +113,14 @@ __device__ __forceinline__ void attn_dimv_body(const AttnParams &p, const int32_
   const rsrc_t vrs = make_rsrc(p.v + b * p.vs0 + g * p.vs1, (int64_t)D * p.vs2 * 2);
   const uint32_t ks2b = (uint32_t)p.ks2 * 2, vs2b = (uint32_t)p.vs2 * 2;
 
-  // Q^T fragment (B operand): lane (ln, hf) holds q[qi][16 ks + 8 hf .. +7]
+  // Q^T fragment (B operand): lane (ln, hf) holds q[qrow][16 ks + 8 hf .. +7],
+  // qrow the row of q holding query qi (through the gather permutation)
+  const int qrow = (qi < N && p.gperm) ? p.gperm[bh * N + qi] : qi;
+  const bool qok = qi < N && qrow >= 0 && qrow < N;
   bf16x8 qf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    const uint32_t off = qi < N ? (uint32_t)(((int64_t)qi * p.qs2 + ks * 16 + hf * 8) * 2) : kOOR;
+    const uint32_t off = qok ? (uint32_t)(((int64_t)qrow * p.qs2 + ks * 16 + hf * 8) * 2) : kOOR;
     qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   }
 

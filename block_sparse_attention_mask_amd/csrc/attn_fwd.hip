@@ -22,7 +22,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   if (a->Hq % a->Hkv) return BSA_ERR_ARG;
   if (a->v_layout != BSA_V_TOKEN_MAJOR && a->v_layout != BSA_V_DIM_MAJOR) return BSA_ERR_ARG;
   if ((a->d != 64 && a->d != 128) || (a->block != 64 && a->block != 128)) return BSA_ERR_UNSUPPORTED;
-  if (a->causal && a->scatter_perm_q) return BSA_ERR_UNSUPPORTED;
+  if (a->causal && (a->scatter_perm_q || a->gather_perm_q)) return BSA_ERR_UNSUPPORTED;
   // CRM rows feed the dim-major kernels and carry no log-weights
   if (a->crm && (a->lw || a->v_layout != BSA_V_DIM_MAJOR)) return BSA_ERR_UNSUPPORTED;
   if (!bsa_aligned16(a->q) || !bsa_aligned16(a->k) || !bsa_aligned16(a->v) || !bsa_aligned16(a->o))
@@ -67,6 +67,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   p.lw = a->lw;
   p.order = a->order;
   p.sperm = a->scatter_perm_q;
+  p.gperm = a->gather_perm_q;
   p.N = a->N;
   p.R = R;
   p.Hq = a->Hq;

@@ -87,12 +87,15 @@ void attn_tokv_kernel(const AttnParams p) {
   const int e0 = p.row_ptr[r], e1 = p.row_ptr[r + 1];
   const int64_t qi = (int64_t)u * BLK + wave * 32 + ln;  // this lane's query position
 
-  // Q^T fragment (B operand): lane (ln, hf) holds q[qi][16 ks + 8 hf .. +7].
+  // Q^T fragment (B operand): lane (ln, hf) holds q[qrow][16 ks + 8 hf .. +7],
+  // qrow the row of q holding query qi (through the gather permutation).
+  const int64_t qrow = (qi < N && p.gperm) ? (int64_t)p.gperm[bh * N + qi] : qi;
+  const bool qok = qi < N && qrow >= 0 && qrow < N;
   bf16x8 qf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     uint4 x = make_uint4(0, 0, 0, 0);
-    if (qi < N) x = ld16(qb + qi * p.qs2 + ks * 16 + hf * 8);
+    if (qok) x = ld16(qb + qrow * p.qs2 + ks * 16 + hf * 8);
     qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 

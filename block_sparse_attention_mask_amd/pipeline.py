@@ -4,7 +4,8 @@ mask / threshold map -> CSR (bsa_csr_count, bsa_csr_fill), or CRM rows
    (bsa_crm_build) with row offsets from their popcounts (bsa_crm_row_ptr);
    or, with a sampler, the mask and log-weights drawn on the device
    (bsa_segment_offsets, bsa_segment_means, bsa_is_sample) before the CSR
--> [cluster labels -> permutations; gather Q, K]        (permuted workloads)
+-> [cluster labels -> permutations; gather K (Q's gather is fused into the
+   attention kernel's load, or done by bsa_permute_rows)]   (permuted workloads)
 -> V gathered (when permuted) and written dim-major (bsa_transpose_rows)
 -> row schedule (bsa_schedule)
 -> attention forward (bsa_attn_fwd), with the inverse query permutation fused
@@ -77,7 +78,7 @@ class StepResult:
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
             v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False,
-            sampler: Optional[dict] = None) -> StepResult:
+            sampler: Optional[dict] = None, fuse_gather: bool = True) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  With
     ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
@@ -106,7 +107,8 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     if dw.permuted:
         perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=stream)
         perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=stream)
-        q = api.permute_rows(dw.q, perm_q, stream=stream)
+        if not fuse_gather:
+            q = api.permute_rows(dw.q, perm_q, stream=stream)
         k = api.permute_rows(dw.k, perm_k, stream=stream)
         if not v_dim_major:
             v = api.permute_rows(dw.v, perm_k, stream=stream)
@@ -128,9 +130,10 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
         attn_events[0].record(s)
+    gperm = perm_q if (dw.permuted and fuse_gather) else None
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
                             want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, crm=crm_rows,
-                            stream=stream)
+                            gather_perm_q=gperm, stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if dw.permuted and not fuse_scatter:

@@ -329,6 +329,10 @@ int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int
  * computed.  scatter_perm_q (optional, int32 [B*Hq][N]): when set, the output
  * of the query at position i is written to position scatter_perm_q[bh][i] of
  * o (and lse), i.e. the inverse permutation is fused into the store.
+ * gather_perm_q (optional, int32 [B*Hq][N]): when set, q is unpermuted and
+ * the query at permuted position i is row gather_perm_q[bh][i] of q (the
+ * query gather fused into the load; an entry outside [0, N) reads zeros).
+ * Neither permutation may be combined with causal (BSA_ERR_UNSUPPORTED).
  * scale <= 0 selects 1/sqrt(d).  A row with an empty list writes O = 0 and
  * LSE = -inf.  Log-weights must be finite or -inf.  crm (optional, device
  * uint32 [R][ceil(nQB/32)], the layout of bsa_crm_build): when set, each
@@ -354,6 +358,7 @@ typedef struct {
   int32_t causal;
   int32_t v_layout; /* BSA_V_TOKEN_MAJOR or BSA_V_DIM_MAJOR */
   const uint32_t *crm; /* CRM rows in place of row_ptr/col, or NULL */
+  const int32_t *gather_perm_q; /* query gather (int32 [B*Hq][N]), or NULL */
 } bsa_attn_args;
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);

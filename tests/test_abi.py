@@ -192,6 +192,7 @@ def _args(**kw):
     (dict(Hq=3), _lib.BSA_ERR_ARG),
     (dict(N=0), _lib.BSA_ERR_ARG),
     (dict(causal=1, scatter_perm_q=FAKE), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(causal=1, gather_perm_q=FAKE), _lib.BSA_ERR_UNSUPPORTED),
     (dict(q=ctypes.c_void_p(4104)), _lib.BSA_ERR_ARG),
     (dict(q_str=_lib.I64x3(4 * 1000 * 128, 1000 * 128, 130)), _lib.BSA_ERR_ARG),
     (dict(o=FAKE), _lib.BSA_ERR_ARG),

@@ -56,7 +56,7 @@ def test_csr_bit_exact(name):
 def test_attention_matches_oracle(name, sched, fuse, vdm):
     w = make(name)
     _log("case %s: attention sched=%s fuse=%s v_dim_major=%s" % (name, sched, fuse, vdm))
-    _, res = run_gpu(w, schedule=sched, fuse_scatter=fuse, n_xcd=8, wave_rows=16, v_dim_major=vdm)
+    _, res = run_gpu(w, schedule=sched, fuse_scatter=fuse, fuse_gather=fuse, n_xcd=8, wave_rows=16, v_dim_major=vdm)
     pq, pk = oracle_perms(w)
     rows = np.arange(w.B * w.Hq * w.N, dtype=np.int64)
     stats = compare_rows(w, res, rows, pq, pk)
@@ -81,10 +81,14 @@ def test_order_invariance_and_determinism(vdm):
     _, r1 = run_gpu(w, schedule=False, fuse_scatter=True, v_dim_major=vdm)
     _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True, v_dim_major=vdm)
     _, r3 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, v_dim_major=vdm)
+    _, r4 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, fuse_gather=False,
+                    v_dim_major=vdm)
     a = r1.out.cpu().numpy()
     assert np.array_equal(a, r2.out.cpu().numpy())
     assert np.array_equal(a, r3.out.cpu().numpy())
+    assert np.array_equal(a, r4.out.cpu().numpy())       # fused query gather == explicit gather
     assert np.array_equal(r1.lse.cpu().numpy(), r3.lse.cpu().numpy())
+    assert np.array_equal(r1.lse.cpu().numpy(), r4.lse.cpu().numpy())
 
 
 @pytest.mark.parametrize("BH,N,C", [(3, 75600, 64), (2, 5000, 1023), (2, 5000, 1024), (1, 9000, 3000),
