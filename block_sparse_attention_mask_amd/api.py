@@ -66,7 +66,10 @@ def device_clock_khz() -> int:
 
 
 def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,
-              row_ptr: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, int]:
+              row_ptr: Optional[torch.Tensor] = None, want_nnz: bool = True,
+              stream=None) -> Tuple[torch.Tensor, Optional[int]]:
+    """bsa_csr_count -> (row_ptr, nnz); with want_nnz=False no host round trip
+    and nnz is None."""
     src = mask if mask is not None else T
     R, nKB = src.shape
     nQB = nKB if nQB is None else nQB
@@ -80,9 +83,9 @@ def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, forc
         row_ptr = torch.empty(R + 1, dtype=torch.int32, device=src.device)
     nnz = I64(0)
     check("bsa_csr_count", load().bsa_csr_count(_ptr(mask), _ptr(T), float(p), R, nQB, nKB,
-                                                int(force_diag), _ptr(row_ptr), ctypes.byref(nnz),
-                                                _stream(stream)))
-    return row_ptr, int(nnz.value)
+                                                int(force_diag), _ptr(row_ptr),
+                                                ctypes.byref(nnz) if want_nnz else None, _stream(stream)))
+    return row_ptr, (int(nnz.value) if want_nnz else None)
 
 
 def csr_fill(row_ptr: torch.Tensor, nnz: int, mask=None, T=None, p: float = 0.0, lw_map=None,
@@ -105,9 +108,16 @@ def csr_fill(row_ptr: torch.Tensor, nnz: int, mask=None, T=None, p: float = 0.0,
 
 
 def build_csr(mask=None, T=None, p: float = 0.0, lw_map=None, nQB: Optional[int] = None,
-              force_diag: bool = True, want_lw: bool = False, stream=None):
-    """bsa_csr_count + allocation + bsa_csr_fill -> (row_ptr, col, lw or None)."""
-    row_ptr, nnz = csr_count(mask, T, p, nQB, force_diag, stream=stream)
+              force_diag: bool = True, want_lw: bool = False, sync: bool = True, stream=None):
+    """bsa_csr_count + allocation + bsa_csr_fill -> (row_ptr, col, lw or None).
+    With sync=False, col (and lw) are sized by the bound R * nKB, so no host
+    round trip is needed; entries past row_ptr[R] are unused."""
+    if sync:
+        row_ptr, nnz = csr_count(mask, T, p, nQB, force_diag, stream=stream)
+    else:
+        row_ptr, _ = csr_count(mask, T, p, nQB, force_diag, want_nnz=False, stream=stream)
+        src = mask if mask is not None else T
+        nnz = src.shape[0] * src.shape[1]
     col, lw = csr_fill(row_ptr, nnz, mask, T, p, lw_map, nQB, force_diag, want_lw, stream=stream)
     return row_ptr, col, lw
 

@@ -165,7 +165,6 @@ extern "C" int bsa_csr_count(const uint8_t *mask, const float *T, float p, int64
                              bsa_stream_t stream) {
   int rc = check_csr_args(mask, T, R, nQB, nKB, force_diag, row_ptr);
   if (rc) return rc;
-  if (!nnz_out) return BSA_ERR_ARG;
   hipStream_t s = bsa_hip_stream(stream);
   if (R > 0) {
     const unsigned grid = (unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock);
@@ -175,10 +174,12 @@ extern "C" int bsa_csr_count(const uint8_t *mask, const float *T, float p, int64
   }
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, row_ptr, R);
   BSA_LAUNCH_CHECK();
-  int32_t n = 0;
-  BSA_HIP(hipMemcpyAsync(&n, row_ptr + R, sizeof(n), hipMemcpyDeviceToHost, s));
-  BSA_HIP(hipStreamSynchronize(s));
-  *nnz_out = n;
+  if (nnz_out) {
+    int32_t n = 0;
+    BSA_HIP(hipMemcpyAsync(&n, row_ptr + R, sizeof(n), hipMemcpyDeviceToHost, s));
+    BSA_HIP(hipStreamSynchronize(s));
+    *nnz_out = n;
+  }
   return BSA_OK;
 }
 

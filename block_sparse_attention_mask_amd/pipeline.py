@@ -62,6 +62,20 @@ def to_device(w, device="cuda") -> DeviceWorkload:
                           int(w.n_clusters), bool(w.causal), bool(w.force_diag))
 
 
+_side_streams = {}
+
+
+def _side_stream(device) -> "torch.cuda.Stream":
+    """A second stream per device (default priority) for the work that can
+    run beside the list building."""
+    key = torch.device(device).index
+    s = _side_streams.get(key)
+    if s is None:
+        s = torch.cuda.Stream(device=device)
+        _side_streams[key] = s
+    return s
+
+
 @dataclass
 class StepResult:
     out: torch.Tensor
@@ -78,13 +92,16 @@ class StepResult:
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
             v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False,
-            sampler: Optional[dict] = None, fuse_gather: bool = True) -> StepResult:
+            sampler: Optional[dict] = None, fuse_gather: bool = True, overlap: bool = False) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  With
     ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
     each head's query blocks (that many subspace iterations).  With ``crm``
     the lists are CRM rows (no log-weights, dim-major V); their sizes are
     known up front, so this path makes no host synchronisation.  With
+    ``overlap`` the permutations, gathers and transposes run on a second
+    stream while the lists and the schedule are built on this one, and the
+    CSR build makes no host round trip (col is sized by its bound).  With
     ``sampler`` = {"m_exact": E, "m_sample": S, "uoff": float64 [B*Hq][G]}
     (a permuted workload) the block mask and log-weights come from the
     group-shared importance sampler over the permuted Q and K instead of
@@ -93,6 +110,9 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     if sampler is not None:
         return _forward_sampled(dw, sampler, schedule, n_xcd, wave_rows, fuse_scatter, want_lse, attn_events,
                                 stream)
+    if overlap and not crm and stage1_iters == 0:
+        return _forward_overlapped(dw, schedule, n_xcd, wave_rows, fuse_scatter, fuse_gather, want_lse,
+                                   attn_events, v_dim_major, stream)
     if crm:
         if dw.lw_map is not None or not v_dim_major:
             raise ValueError("CRM lists carry no log-weights and need dim-major V")
@@ -176,6 +196,54 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
         attn_events[1].record(s)
     if not fuse_scatter:
         out = api.unpermute_rows(out, perm_q, stream=stream)
+        if lse is not None:
+            inv = torch.empty_like(lse)
+            inv.scatter_(1, perm_q.long(), lse)
+            lse = inv
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)
+
+
+def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_rows: int, fuse_scatter: bool,
+                        fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream) -> StepResult:
+    """The same step with two streams: [labels -> perms, K (and Q) gathers, V
+    gather + transpose] on a side stream beside [mask -> CSR without a host
+    round trip, schedule] on the caller's stream; attention waits for both."""
+    main = stream if stream is not None else torch.cuda.current_stream()
+    side = _side_stream(dw.q.device)
+    side.wait_stream(main)
+    q, k, v = dw.q, dw.k, dw.v
+    perm_q = perm_k = None
+    with torch.cuda.stream(side):
+        if dw.permuted:
+            perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=side)
+            perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=side)
+            if not fuse_gather:
+                q = api.permute_rows(dw.q, perm_q, stream=side)
+            k = api.permute_rows(dw.k, perm_k, stream=side)
+            if not v_dim_major:
+                v = api.permute_rows(dw.v, perm_k, stream=side)
+        if v_dim_major:
+            v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=side)
+    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag, sync=False,
+                                     stream=main)
+    order = None
+    if schedule:
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main)
+    main.wait_stream(side)
+    for t in (perm_q, perm_k, q, k, v):
+        if t is not None:
+            t.record_stream(main)
+    sperm = perm_q if (dw.permuted and fuse_scatter) else None
+    gperm = perm_q if (dw.permuted and fuse_gather) else None
+    if attn_events is not None:
+        attn_events[0].record(main)
+    out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
+                            want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major,
+                            gather_perm_q=gperm, stream=main)
+    if attn_events is not None:
+        attn_events[1].record(main)
+    if dw.permuted and not fuse_scatter:
+        out = api.unpermute_rows(out, perm_q, stream=main)
         if lse is not None:
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)

@@ -66,8 +66,10 @@ const char *bsa_strerror(int code);
  * empty).  Exactly one of mask (uint8, device) and T (float32, device) must be
  * non-NULL; both are [R][nKB] row-major.
  *
- * Writes row_ptr[0..R] (device, int32, caller-owned, R + 1 entries) and stores
- * nnz = row_ptr[R] into *nnz_out (host).  Synchronises `stream`.
+ * Writes row_ptr[0..R] (device, int32, caller-owned, R + 1 entries).  When
+ * nnz_out != NULL, stores nnz = row_ptr[R] into *nnz_out (host) and
+ * synchronises `stream`; with nnz_out == NULL the call is asynchronous (a
+ * caller that sizes col by the bound R * nKB needs no host round trip).
  * Errors: BSA_ERR_ARG for NULL/negative sizes or both/neither sources;
  * BSA_ERR_UNSUPPORTED when R * nKB >= 2^31 or force_diag with nQB > nKB.
  * ------------------------------------------------------------------------- */

@@ -51,7 +51,6 @@ def test_csr_argument_errors(L):
     assert L.bsa_csr_count(FAKE, FAKE, 0.5, 4, 2, 2, 1, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
     assert L.bsa_csr_count(FAKE, None, 0.5, -1, 2, 2, 1, FAKE, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
     assert L.bsa_csr_count(FAKE, None, 0.5, 4, 2, 2, 1, None, ctypes.byref(n), None) == _lib.BSA_ERR_ARG
-    assert L.bsa_csr_count(FAKE, None, 0.5, 4, 2, 2, 1, FAKE, None, None) == _lib.BSA_ERR_ARG
     assert L.bsa_csr_count(FAKE, None, 0.5, 1 << 30, 4, 4, 1, FAKE, ctypes.byref(n), None) == \
         _lib.BSA_ERR_UNSUPPORTED
     assert L.bsa_csr_count(FAKE, None, 0.5, 4, 3, 2, 1, FAKE, ctypes.byref(n), None) == \

@@ -91,6 +91,20 @@ def test_order_invariance_and_determinism(vdm):
     assert np.array_equal(r1.lse.cpu().numpy(), r4.lse.cpu().numpy())
 
 
+@pytest.mark.parametrize("name", ["b128_d128_perm_lw", "b64_d64_gqa_T", "b128_d128_causal_gqa"])
+def test_overlapped_step_is_bit_identical(name):
+    """The two-stream step (CSR without a host round trip) gives the same bits
+    as the one-stream step."""
+    w = make(name)
+    _log("case overlapped step %s" % name)
+    _, r1 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0)
+    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, overlap=True)
+    nnz = int(r1.row_ptr[-1].item())
+    assert torch.equal(r1.row_ptr, r2.row_ptr) and torch.equal(r1.col, r2.col[:nnz])
+    assert torch.equal(r1.order, r2.order)
+    assert torch.equal(r1.out, r2.out) and torch.equal(r1.lse, r2.lse)
+
+
 @pytest.mark.parametrize("BH,N,C", [(3, 75600, 64), (2, 5000, 1023), (2, 5000, 1024), (1, 9000, 3000),
                                     (4, 17, 5), (2, 64 * 16 * 8 + 1, 7)])
 def test_perm_from_labels_bit_exact(BH, N, C):
