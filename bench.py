@@ -406,7 +406,8 @@ def device_info(torch):
     from block_sparse_attention_mask_amd import api
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": p.gcnArchName, "cus": api.device_cus(),
-            "peak_sclk_mhz": api.device_clock_khz() // 1000}
+            "peak_sclk_mhz": api.device_clock_khz() // 1000,
+            "sclk_mhz_under_mfma_load": api.clock_under_mfma_load()}
 
 
 def traffic_bytes(cfg):
@@ -496,7 +497,9 @@ def cpu_baseline(w, rp, col, res, target_s, metrics):
     return {"value": value, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
             "sample": "%d seeded random query rows of the same workload (all heads), fp64 "
                       "dense-masked oracle, %.1f s" % (n, dt),
-            "seconds": round(dt, 3), "rows": n}
+            "seconds": round(dt, 3), "rows": n, "rows_per_s": round(n / dt, 1),
+            "extrapolated_full_seconds": round(dt * total_rows / n, 1),
+            "extrapolation": "sample time x all query rows / sampled rows (rows of equal expected work)"}
 
 
 def row_pairs_causal(rp, col, r, t, w):

@@ -24,7 +24,7 @@ EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_
            "bsa_crm_to_csr", "bsa_segment_offsets", "bsa_segment_means", "bsa_is_sample", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
            "bsa_attn_fwd", "bsa_attn_tok_fwd",
-           "bsa_device_cus", "bsa_device_clock_khz")
+           "bsa_device_cus", "bsa_device_clock_khz", "bsa_clock_probe")
 
 
 class AttnArgs(ctypes.Structure):
@@ -111,6 +111,8 @@ def load():
         L.bsa_spectral_order.argtypes = [P, P, I32, I32, I32, I32, P, P, P]
         L.bsa_attn_fwd.restype = ctypes.c_int
         L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
+        L.bsa_clock_probe.restype = ctypes.c_int
+        L.bsa_clock_probe.argtypes = [I32, I32, P, P]
         L.bsa_attn_tok_fwd.restype = ctypes.c_int
         L.bsa_attn_tok_fwd.argtypes = [ctypes.POINTER(TokArgs), P]
         L.bsa_device_cus.restype = ctypes.c_int

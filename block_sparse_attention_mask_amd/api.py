@@ -65,6 +65,19 @@ def device_clock_khz() -> int:
     return k
 
 
+def clock_under_mfma_load(blocks: int = 0, iters: int = 20000, stream=None) -> dict:
+    """bsa_clock_probe over every CU (4 workgroups per CU by default):
+    median, min and max engine clock in MHz of the wavefronts."""
+    if blocks <= 0:
+        blocks = 4 * device_cus()
+    ticks = torch.zeros(4 * blocks * 2, dtype=torch.int64, device="cuda")
+    check("bsa_clock_probe", load().bsa_clock_probe(int(blocks), int(iters), _ptr(ticks), _stream(stream)))
+    torch.cuda.synchronize()
+    t = ticks.cpu().numpy().reshape(-1, 2).astype("float64")
+    mhz = sorted(t[:, 0] / t[:, 1] * 100.0)
+    return {"median": round(mhz[len(mhz) // 2], 1), "min": round(mhz[0], 1), "max": round(mhz[-1], 1)}
+
+
 def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,
               row_ptr: Optional[torch.Tensor] = None, want_nnz: bool = True,
               stream=None) -> Tuple[torch.Tensor, Optional[int]]:

@@ -411,6 +411,18 @@ typedef struct {
 
 int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Engine-clock probe under MFMA load (for reading a measurement against the
+ * clock the device sustains, not the path itself).  Launches `blocks`
+ * workgroups of four wavefronts; each wavefront runs `iters` iterations of
+ * four independent 32x32x16 bf16 MFMA chains and writes, at ticks[2w] and
+ * ticks[2w + 1] (device uint64 [4 * blocks][2], caller-owned), how far the
+ * shader clock counter and the 100 MHz real-time counter advanced; the
+ * wavefront's clock is ticks[2w] / ticks[2w + 1] * 100 MHz.  BSA_ERR_ARG for
+ * NULL or non-positive sizes.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_clock_probe(int32_t blocks, int32_t iters, uint64_t *ticks, bsa_stream_t stream);
+
 /* Number of compute units of the current device (for wave sizing), or a
  * negative error. */
 int bsa_device_cus(void);

@@ -98,6 +98,12 @@ def test_spectral_order_argument_errors(L):
     assert L.bsa_spectral_order(FAKE, FAKE, 4, 700, 700, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
 
 
+def test_clock_probe_argument_errors(L):
+    assert L.bsa_clock_probe(4, 100, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_clock_probe(0, 100, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_clock_probe(4, 0, FAKE, None) == _lib.BSA_ERR_ARG
+
+
 def test_crm_argument_errors(L):
     n = _lib.I64(0)
     assert L.bsa_crm_build(None, None, 0.5, 4, 2, 2, 1, FAKE, None) == _lib.BSA_ERR_ARG
