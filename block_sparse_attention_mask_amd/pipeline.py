@@ -205,9 +205,10 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
 
 def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_rows: int, fuse_scatter: bool,
                         fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream) -> StepResult:
-    """The same step with two streams: [labels -> perms, K (and Q) gathers, V
-    gather + transpose] on a side stream beside [mask -> CSR without a host
-    round trip, schedule] on the caller's stream; attention waits for both."""
+    """The same step with two streams: [key labels -> perm_k, K gather, V
+    gather + transpose] on a side stream beside [query labels -> perm_q,
+    mask -> CSR without a host round trip, schedule] on the caller's stream;
+    attention waits for both."""
     main = stream if stream is not None else torch.cuda.current_stream()
     side = _side_stream(dw.q.device)
     side.wait_stream(main)
@@ -215,22 +216,25 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
     perm_q = perm_k = None
     with torch.cuda.stream(side):
         if dw.permuted:
-            perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=side)
             perm_k = api.perm_from_labels(dw.labels_k, dw.n_clusters, stream=side)
-            if not fuse_gather:
-                q = api.permute_rows(dw.q, perm_q, stream=side)
             k = api.permute_rows(dw.k, perm_k, stream=side)
             if not v_dim_major:
                 v = api.permute_rows(dw.v, perm_k, stream=side)
         if v_dim_major:
             v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=side)
+    # the query permutation is only needed by the attention launch (or the
+    # explicit Q gather), so it is built here, beside the K/V work
+    if dw.permuted:
+        perm_q = api.perm_from_labels(dw.labels_q, dw.n_clusters, stream=main)
+        if not fuse_gather:
+            q = api.permute_rows(dw.q, perm_q, stream=main)
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag, sync=False,
                                      stream=main)
     order = None
     if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main)
     main.wait_stream(side)
-    for t in (perm_q, perm_k, q, k, v):
+    for t in (perm_k, k, v):
         if t is not None:
             t.record_stream(main)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
