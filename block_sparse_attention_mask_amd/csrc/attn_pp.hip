@@ -40,10 +40,11 @@
 //     per PV k-step are eight consecutive keys and the V^T operand is one
 //     16-byte read.
 //   * Softmax in base 2, fp32, p = 2^(c s + lw - m) with c = log2(e)/sqrt(d).
-//     No per-tile max is taken: the running max m (starting at 0) is raised,
+//     No per-tile max is taken: the running max m (starting at 0) is moved,
 //     O and l rescaled and the tile's exponentials redone, only when a
 //     lane's 32 probabilities of the tile sum past 32 * 2^8 (so some
-//     probability exceeded 2^8) or nothing has been accumulated yet.
+//     probability exceeded 2^8), or while the lane's sum so far is below
+//     2^-64 (nothing accumulated, or only underflowing probabilities).
 //   * The row's list is staged in LDS, up to 1024 entries at a time: copied
 //     from the CSR column array, or walked out of the row's CRM words
 //     (ScalingAttention, section 7.3) with each wavefront taking a 4-bit
@@ -308,9 +309,9 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           for (int e = 0; e < 16; ++e)
             if (32 * jj + 16 * (e >> 3) + (e & 7) >= lim) s[jj][e] = -INFINITY;
       }
-      // exponentials against the running max; it is raised only when a lane's
+      // exponentials against the running max; it is moved only when a lane's
       // 32 probabilities sum past 32 * 2^8 (some probability above 2^8) or
-      // nothing has been accumulated yet, and then the tile is redone
+      // the lane's sum so far is below 2^-64, and then the tile is redone
       float nb = bias - m_run;
       float ls = 0.f;
 #pragma unroll
@@ -329,7 +330,7 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           for (int t = gi * C::NSLOT / (2 * C::MTW); t < (gi + 1) * C::NSLOT / (2 * C::MTW); ++t)
             copy_slot(t, kd, vd, sr);
         }
-      if (__any(ls > 32.f * 256.f || l_run + ls == 0.f)) {
+      if (__any(ls > 32.f * 256.f || l_run + ls < 0x1p-64f)) {
         float m = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < C::MTW; ++jj)
@@ -337,10 +338,17 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
           for (int e = 0; e < 16; ++e) m = fmaxf(m, fmaf(s[jj][e], p.c, nb));
         m = halves_max(m);
         const float lsum = halves_sum(ls), lrun = halves_sum(l_run);
-        const float sh = (m > kTau || (lrun + lsum == 0.f && m > -INFINITY)) ? m : 0.f;
+        // Raised when a probability may exceed 2^8.  While the sum so far
+        // (this tile included) is below 2^-64 (nothing, or only denormal
+        // probabilities), moved toward the tile max: all the way when nothing
+        // has been accumulated (O and l are zero and are multiplied by 0), by
+        // at most 64 otherwise, so the rescale factor stays finite.
+        float sh = 0.f;
+        if (m > kTau) sh = m;
+        else if (lrun + lsum < 0x1p-64f && m > -INFINITY) sh = lrun == 0.f ? m : fmaxf(m, -64.f);
         m_run += sh;
         nb = bias - m_run;
-        const float alpha = __builtin_amdgcn_exp2f(-sh);
+        const float alpha = lrun == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
@@ -468,9 +476,13 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     if (KH != 0) return;
     const float m2 = mrg_ml[qg][0][lane];
     const float l2 = mrg_ml[qg][1][lane];
-    const float m = fmaxf(m_run, m2);
-    const float a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
+    // A half with nothing accumulated (l = 0) takes no part, whatever running
+    // max it holds: its max may sit far above the other half's (a fully
+    // masked half keeps its starting max of 0 while the other half's scores
+    // are far below it), and a weight 2^(m_other - m) would then underflow.
+    const float m = l_w > 0.f ? (l2 > 0.f ? fmaxf(m_run, m2) : m_run) : m2;
+    const float a1 = l_w > 0.f ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
+    const float a2 = l2 > 0.f ? __builtin_amdgcn_exp2f(m2 - m) : 0.f;
     const float l_tot = l_w * a1 + l2 * a2;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int oi = (qi < N && sperm) ? sperm[bh * N + qi] : qi;

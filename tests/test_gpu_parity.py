@@ -177,6 +177,27 @@ def test_zero_queries_and_constant_values():
     assert np.abs(bf16_tensor_to_f32(res.out) - np.float32(0.625)).max() <= 2.0 ** -8
 
 
+@pytest.mark.parametrize("block,causal,vdm", [(128, True, True), (128, False, True), (64, True, True),
+                                            (128, True, False)])
+def test_underflowing_scores_with_an_empty_key_half(block, causal, vdm):
+    """Every score at about -130 in base-2 units (all keys equal, every query
+    -8 times that key), each row listing only its diagonal block.  Under the
+    causal mask the first half of each query block has no allowed key in the
+    upper half of the tile, and the partial last block (50 tokens) has none
+    without it: a key range with nothing accumulated must not take part in
+    the merge, whatever running max it holds.  The softmax is uniform over the
+    allowed keys, so O is their mean of V."""
+    w = synth.random_case(77 + block + causal, B=1, Hq=2, Hkv=2, N=2 * 128 + 50, d=128, block=block,
+                          density=0.0, causal=causal)
+    w.k[:] = synth.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    w.q[:] = synth.f32_to_bf16_bits(np.array([-8.0], np.float32))[0]
+    _log("case underflowing scores block=%d causal=%d v_dim_major=%d" % (block, causal, vdm))
+    _, res = run_gpu(w, schedule=False, v_dim_major=vdm)
+    stats = compare_rows(w, res, np.arange(2 * w.N, dtype=np.int64))
+    _log("  %s" % stats)
+    assert_within(stats)
+
+
 @pytest.mark.parametrize("block,d,nblocks", [(128, 128, 1100), (64, 64, 1100)])
 def test_long_rows_span_list_chunks(block, d, nblocks):
     """Rows of over a thousand KV blocks: the kernels stage a row's CSR list in
