@@ -45,6 +45,10 @@ def parse():
                          "so that a profile holds only the headline kernel's launches")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for HBM counter scaling)")
+    ap.add_argument("--dense-launches", type=int, default=0,
+                    help="instead of the step: launch the attention kernel this many times on dense "
+                         "1x40x16384 heads (every 128x128 block listed), print the median, and exit "
+                         "(a short, fixed program for counter passes)")
     ap.add_argument("--n-xcd", type=int, default=8)
     ap.add_argument("--wave-rows", type=int, default=0)
     return ap.parse_args()
@@ -52,6 +56,34 @@ def parse():
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def dense_launches(torch, n):
+    """Dense 1 x 40 x 16384 heads, d = 128, every 128x128 block listed, V
+    dim-major, longest-first schedule: n launches of the attention kernel,
+    each timed with HIP events on the current stream; prints the median."""
+    from block_sparse_attention_mask_amd import api
+    H, N = 40, 16384
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q, k, v = (torch.randn(1, H, N, 128, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    vt = api.transpose_rows(v)
+    nb = N // 128
+    rp, col, _ = api.build_csr(torch.ones(H * nb, nb, dtype=torch.uint8, device="cuda"), nQB=nb)
+    order = api.schedule(rp, 1, H, H, nb, 2048, 8)
+    out = torch.empty_like(q)
+    s = torch.cuda.current_stream()
+    ms = []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        api.attn_fwd(q, k, vt, rp, col, 128, order=order, out=out, v_dim_major=True)
+        b.record(s)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    t = float(np.median(ms))
+    flop = 4.0 * 128 * H * N * N
+    print(json.dumps({"workload": "dense 1x40x16384, d128, 128x128 blocks", "launches": n, "median_ms": round(t, 4),
+                      "tflops": round(flop / (t * 1e-3) / 1e12, 2)}))
 
 
 def main():
@@ -69,6 +101,9 @@ def main():
         raise SystemExit("no GPU visible")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dense_launches:
+        dense_launches(torch, args.dense_launches)
+        return
 
     t0 = time.time()
     w = synth.CONFIGS[args.config]()
