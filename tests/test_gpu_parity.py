@@ -198,6 +198,28 @@ def test_underflowing_scores_with_an_empty_key_half(block, causal, vdm):
     assert_within(stats)
 
 
+@pytest.mark.parametrize("block,vdm", [(128, True), (64, True), (128, False)])
+def test_scores_far_above_the_running_max(block, vdm):
+    """Every row lists every block; the keys of block v are (v mod 3 + 1)
+    times a fixed key and every query is 8 times that key, so a row's scores
+    sit near 130, 260 and 390 (base 2) by block.  The first exponentials
+    overflow, later blocks raise the running max by far more than the
+    exponent range after something has been accumulated, and the rescale
+    factor of the earlier blocks underflows to zero.  The softmax then puts
+    all its weight on the keys of the top blocks, whose scores are equal."""
+    N = 5 * block + 23
+    w = synth.random_case(91 + block, B=1, Hq=2, Hkv=1, N=N, d=128, block=block, density=2.0)
+    k0 = synth.f32_to_bf16_bits(np.array([1.0, 2.0, 3.0], np.float32))
+    for v in range(-(-N // block)):
+        w.k[:, :, v * block:(v + 1) * block] = k0[v % 3]
+    w.q[:] = synth.f32_to_bf16_bits(np.array([8.0], np.float32))[0]
+    _log("case scores far above the running max block=%d v_dim_major=%d" % (block, vdm))
+    _, res = run_gpu(w, schedule=True, n_xcd=8, v_dim_major=vdm)
+    stats = compare_rows(w, res, np.arange(2 * w.N, dtype=np.int64))
+    _log("  %s" % stats)
+    assert_within(stats)
+
+
 @pytest.mark.parametrize("block,d,nblocks", [(128, 128, 1100), (64, 64, 1100)])
 def test_long_rows_span_list_chunks(block, d, nblocks):
     """Rows of over a thousand KV blocks: the kernels stage a row's CSR list in

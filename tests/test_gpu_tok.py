@@ -122,3 +122,31 @@ def test_token_selection():
     slots = np.sort(rng.choice(B * Hq * C * 128, size=3000, replace=False)).astype(np.int64)
     _log("case tok token selection N=%d keys=1500" % N)
     _run_and_compare(q, k, v, *maps, False, "token selection", slots)
+
+
+def test_extreme_scores():
+    """Keys scaled by 1, 2 or 3 in runs of 256 tokens and every query +-8 times
+    the same fixed key: scores near +-130, 260 and 390 (base 2).  Head 0's
+    softmax puts its weight on the largest-scaled keys of each list; head 1's
+    (negative queries) on the smallest-scaled ones, with every score far
+    below zero.  Random lists of every awkward length, causal and not."""
+    B, Hq, Hkv, N, BQ = 1, 2, 1, 3000, 64
+    _, _, v = _qkv(71, B, Hq, Hkv, N)
+    scale = 1.0 + (np.arange(N) // 256) % 3
+    one = np.ones(128, np.float32)
+    k = synth.f32_to_bf16_bits((scale[:, None] * one[None, :]).astype(np.float32)).reshape(B, Hkv, N, 128)
+    q = np.empty((B, Hq, N, 128), np.uint16)
+    q[0, 0] = synth.f32_to_bf16_bits(np.float32(8.0))
+    q[0, 1] = synth.f32_to_bf16_bits(np.float32(-8.0))
+    g = np.random.default_rng(72)
+    C = 8
+    q_idx = np.full((B * Hq, C, BQ), -1, np.int32)
+    for h in range(B * Hq):
+        q_idx[h] = g.permutation(N)[:C * BQ].reshape(C, BQ)
+    lens = [1, 63, 64, 65, 300, 700, 129, 17]
+    lists = [g.integers(0, N, size=lens[c]).astype(np.int32) for h in range(B * Hq) for c in range(C)]
+    kv_ptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    kv_idx = np.concatenate(lists).astype(np.int32)
+    for causal in (False, True):
+        _log("case tok extreme scores causal=%d" % causal)
+        _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, "extreme scores")
