@@ -409,6 +409,10 @@ def token_set_stage(torch):
     maps = synth.cqs_per_head(synth.cqs_scatter(N, R, 128, True), Hq)
     timed("intra_scatter_llama3_8b_32k_sets128", "same, 128-query sets",
           *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
+    # INTRA Gather 1 on the same shape: segments of 8 tokens dealt cyclically to 8 groups, causal
+    maps = synth.cqs_per_head(synth.cqs_gather1(N, R, 64, True), Hq)
+    timed("intra_gather1_llama3_8b_32k", "1x32q/8kv x 32768, d128, 8 groups of cyclic 8-token segments, causal, "
+          "64-query sets", *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
     del qkv_s
     # INTRA Gather 0, FLUX.1-dev 2048x2048 image (128x128 tokens): 8x8 patches, 16x16 windows
     H = W = 128

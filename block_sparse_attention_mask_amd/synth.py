@@ -449,6 +449,25 @@ def cqs_scatter(N: int, R: int = 8, BQ: int = 64, causal: bool = False):
     return _lists_to_csr(qsets, ksets, BQ)
 
 
+def cqs_gather1(N: int, R: int = 8, BQ: int = 64, causal: bool = False):
+    """INTRA Gather 1 (appendix: the repeated-segment token grouping of the
+    token-level benchmarks; the cyclic Gather of the relay analysis), read as:
+    the sequence splits into segments of R consecutive tokens (the
+    neighbourhoods Scatter takes one token from), and segment p joins group
+    p mod R, so group b holds the segments b, b + R, b + 2R, ...  Each query
+    set is BQ consecutive members of one group and its keys are the group's
+    members (when causal, only those up to the set's last query).  Returns
+    (q_idx [C][BQ], kv_ptr [C+1], kv_idx) for one head."""
+    qsets, ksets = [], []
+    seg = np.arange(N) // R
+    for b in range(R):
+        members = np.nonzero(seg % R == b)[0]
+        for b0 in range(0, len(members), BQ):
+            qsets.append(members[b0:b0 + BQ])
+            ksets.append(members[:b0 + BQ] if causal else members)
+    return _lists_to_csr(qsets, ksets, BQ)
+
+
 def cqs_gather0(H: int, W: int):
     """INTRA Gather 0 (appendix, sparse pattern index functions): query set i
     is the 8x8 patch (r, c) = divmod(i, W / 8) of an H x W token image

@@ -5,7 +5,7 @@ C ABI, against the oracle on the same seeded inputs.
 Cases: random sets with lists of every awkward length (empty, 1, 63, 64,
 65, over a 1024-entry staging chunk), out-of-range and duplicate entries,
 empty query slots, GQA, full and causal masking, 64- and 128-query sets;
-INTRA's Scatter and Gather 0 maps; a token-selection workload of MC-Sparse's
+INTRA's Scatter, Gather 1 and Gather 0 maps; a token-selection workload of MC-Sparse's
 shape.  Bar: max-abs 2e-2, mean-abs 2e-3 on O, 1e-3 on LSE; rows that no set
 lists stay untouched.
 """
@@ -102,6 +102,15 @@ def test_intra_scatter(causal):
     maps = synth.cqs_per_head(synth.cqs_scatter(N, 8, 64, causal), B * Hq)
     _log("case tok INTRA Scatter N=%d causal=%d" % (N, causal))
     _run_and_compare(q, k, v, *maps, causal, "scatter")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_intra_gather1(causal):
+    B, Hq, Hkv, N = 1, 4, 2, 4096 + 40
+    q, k, v = _qkv(23 + causal, B, Hq, Hkv, N)
+    maps = synth.cqs_per_head(synth.cqs_gather1(N, 8, 64, causal), B * Hq)
+    _log("case tok INTRA Gather 1 N=%d causal=%d" % (N, causal))
+    _run_and_compare(q, k, v, *maps, causal, "gather1")
 
 
 def test_intra_gather0():

@@ -10,8 +10,10 @@ and of the query-set index maps.
 * Closed forms: constant V gives that constant; an empty list gives O = 0,
   LSE = -inf; an empty slot gives NaN.
 * Index maps: INTRA Scatter covers every token once and lists each group's
-  members; Gather 0 lists 256 distinct in-image keys per patch, in four
-  tiles of four rows of 16, containing the patch, shifted inward at edges.
+  members; Gather 1 (cyclic segments) covers every token once, lists whole
+  segments, and meets every Scatter group in exactly T / R tokens; Gather 0
+  lists 256 distinct in-image keys per patch, in four tiles of four rows of
+  16, containing the patch, shifted inward at edges.
 """
 import numpy as np
 import pytest
@@ -134,6 +136,29 @@ def test_scatter_map_covers_every_token_once():
             members = np.arange(r, N, R)
             want = members[members <= qc.max()] if causal else members
             np.testing.assert_array_equal(keys, want)
+
+
+@pytest.mark.parametrize("N,R,causal", [(4096, 8, False), (4096, 8, True), (1000, 8, True), (777, 4, False)])
+def test_gather1_map_is_cyclic_segments(N, R, causal):
+    q_idx, kv_ptr, kv_idx = synth.cqs_gather1(N, R, 64, causal)
+    qs = q_idx[q_idx >= 0]
+    np.testing.assert_array_equal(np.sort(qs), np.arange(N))          # every token in exactly one set
+    for c in range(q_idx.shape[0]):
+        qc = q_idx[c][q_idx[c] >= 0]
+        b = (qc[0] // R) % R
+        assert np.all((qc // R) % R == b)                              # one group per set
+        members = np.array([t for t in range(N) if (t // R) % R == b])
+        keys = kv_idx[kv_ptr[c]:kv_ptr[c + 1]]
+        np.testing.assert_array_equal(keys, members[members <= qc.max()] if causal else members)
+    # the relay property of the cyclic Gather: with N = T R and T a multiple
+    # of R, every Gather group shares exactly T / R tokens with every Scatter
+    # group (local index t mod R)
+    if N % (R * R) == 0:
+        T = N // R
+        groups = [np.array([t for t in range(N) if (t // R) % R == b]) for b in range(R)]
+        for b in range(R):
+            for r in range(R):
+                assert np.sum(groups[b] % R == r) == T // R
 
 
 @pytest.mark.parametrize("H,W", [(16, 16), (32, 48), (64, 64)])
