@@ -68,6 +68,11 @@ def lib():
                                        I64, P, P, P]
         L.oracle_count_pairs.restype = I64
         L.oracle_count_pairs.argtypes = [P, P, I64, I64, I64, ctypes.c_int]
+        L.oracle_group_mass.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64, P, ctypes.c_int,
+                                        ctypes.c_double, I64, I64, P]
+        L.oracle_group_mass.restype = ctypes.c_int
+        L.oracle_topk.argtypes = [P, I64, I64, I64, P]
+        L.oracle_topk.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -299,3 +304,41 @@ def attn_full(w, row_ptr, col, lw, perm_q=None, perm_k=None, rows=None):
     if rows is None:
         rows = np.arange(w.B * w.Hq * w.N, dtype=np.int64)
     return attn_rows(w.q, w.k, w.v, row_ptr, col, lw, w.block, rows, perm_q, perm_k, w.causal)
+
+
+def group_mass(q, k, q_idx, causal: bool = False, scale: Optional[float] = None, keys=None):
+    """MC-Sparse's exact selection, second pass: per query group (q_idx int32
+    [B*Hq][C][BQ], empty slots outside [0, N)), the sum over the group's
+    queries of each key's attention probability under the dense softmax
+    (causal: keys after the query excluded).  keys = (s0, s1) restricts the
+    output columns.  Returns float64 [B*Hq*C][s1 - s0]."""
+    q, k = np.asarray(q), np.asarray(k)
+    for a in (q, k):
+        assert a.dtype == np.uint16 and a.strides[-1] == 2
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    q_idx = np.ascontiguousarray(q_idx, dtype=np.int32)
+    C, BQ = q_idx.shape[1], q_idx.shape[2]
+    s0, s1 = (0, N) if keys is None else keys
+    st = lambda a: np.array([s // 2 for s in a.strides[:3]], dtype=np.int64)
+    out = np.empty((B * Hq * C, s1 - s0), dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rc = lib().oracle_group_mass(_p(q), _p(k), _p(st(q)), _p(st(k)), B, Hq, Hkv, N, d, C, BQ, _p(q_idx),
+                                 int(causal), float(scale), int(s0), int(s1), _p(out))
+    if rc:
+        raise ValueError("oracle_group_mass failed: %d" % rc)
+    return out
+
+
+def topk(mass, K: int) -> np.ndarray:
+    """The K largest of each row (ties to the lower index), ascending indices:
+    int32 [rows][min(K, N)].  float32 input is widened exactly."""
+    mass = np.ascontiguousarray(np.asarray(mass, dtype=np.float64))
+    rows, N = mass.shape
+    k = min(K, N)
+    idx = np.empty((rows, k), dtype=np.int32)
+    rc = lib().oracle_topk(_p(mass), rows, N, int(K), _p(idx))
+    if rc:
+        raise ValueError("oracle_topk failed: %d" % rc)
+    return idx

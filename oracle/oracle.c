@@ -70,6 +70,13 @@
  *                     CQS's key list, one term per list entry; entries
  *                     outside the sequence and, when causal, keys after the
  *                     query are left out.
+ *  oracle_group_mass  MC-Sparse's exact token selection, second pass: the
+ *                     attention probabilities of every query of a group
+ *                     (softmax over all keys, the dense first pass's LSE)
+ *                     summed per key over the group's queries.
+ *  oracle_topk        The K keys of largest mass per row (MC-Sparse's top-K
+ *                     on the aggregated mass), ties to the lower index,
+ *                     listed in ascending order.
  *  oracle_count_pairs Number of allowed (query, key) token pairs; the FLOP
  *                     convention of 4*d per pair is the one behind INTRA's
  *                     GFLOPS column (INTRA, Table 1 and the overhead table).
@@ -795,4 +802,90 @@ int oracle_attn_tok(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     free(acc);
   }
   return bad ? OR_ERR_ARG : OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MC-Sparse exact token selection                                          */
+/* ------------------------------------------------------------------------ */
+/* Group mass (MC-Sparse, implementation details: a first dense pass gives
+ * each query's log-sum-exp, a second recomputes the scores, recovers the
+ * probabilities and aggregates them per query group).  For group c of head
+ * bh (query positions q_idx[(bh*C + c)*BQ + i], a position outside [0, N)
+ * being an empty slot) and key s in [s0, s1):
+ *   mass = sum over the group's queries t (s <= t when causal) of
+ *          exp(x_ts - LSE_t),  x_ts = scale * Q[t] . K[s],
+ *   LSE_t = ln sum over all keys s' of the query (s' <= t when causal) of
+ *           exp(x_ts').
+ * Output mass[(bh*C + c)*(s1 - s0) + (s - s0)], fp64. */
+int oracle_group_mass(const uint16_t *q, const uint16_t *k, const int64_t *q_str, const int64_t *k_str, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t C, int64_t BQ, const int32_t *q_idx,
+                      int causal, double scale, int64_t s0, int64_t s1, double *mass) {
+  if (!q || !k || !q_idx || !mass) return OR_ERR_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N <= 0 || d <= 0 || C <= 0 || BQ <= 0) return OR_ERR_ARG;
+  if (s0 < 0 || s1 > N || s0 > s1) return OR_ERR_ARG;
+  int64_t G = Hq / Hkv, W = s1 - s0;
+#pragma omp parallel
+  {
+    double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *x = (double *)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t cq = 0; cq < B * Hq * C; ++cq) {
+      int64_t bh = cq / C, b = bh / Hq, h = bh % Hq, g = h / G;
+      double *out = mass + cq * W;
+      for (int64_t s = 0; s < W; ++s) out[s] = 0.0;
+      for (int64_t i = 0; i < BQ; ++i) {
+        int64_t t = q_idx[cq * BQ + i];
+        if (t < 0 || t >= N) continue;
+        const uint16_t *qrow = q + b * q_str[0] + h * q_str[1] + t * q_str[2];
+        for (int64_t c = 0; c < d; ++c) qv[c] = bf16_to_double(qrow[c]);
+        int64_t smax = causal ? t + 1 : N;   /* keys [0, smax) take part */
+        double m = -INFINITY;
+        for (int64_t s = 0; s < smax; ++s) {
+          const uint16_t *krow = k + b * k_str[0] + g * k_str[1] + s * k_str[2];
+          double dot = 0.0;
+          for (int64_t c = 0; c < d; ++c) dot += qv[c] * bf16_to_double(krow[c]);
+          x[s] = scale * dot;
+          if (x[s] > m) m = x[s];
+        }
+        double Z = 0.0;
+        for (int64_t s = 0; s < smax; ++s) Z += exp(x[s] - m);
+        double lse = m + log(Z);
+        for (int64_t s = s0; s < s1 && s < smax; ++s) out[s - s0] += exp(x[s] - lse);
+      }
+    }
+    free(qv);
+    free(x);
+  }
+  return OR_OK;
+}
+
+/* The K largest of each row of mass[rows][N] (MC-Sparse: top-K on the
+ * aggregated attention mass), ties broken toward the lower index; written
+ * to idx[rows][min(K, N)] in ascending index order. */
+static const double *topk_base;
+static int topk_cmp(const void *a, const void *b) {
+  int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+  double x = topk_base[i], y = topk_base[j];
+  if (x > y) return -1;
+  if (x < y) return 1;
+  return (i > j) - (i < j);
+}
+static int asc_cmp(const void *a, const void *b) {
+  int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+  return (i > j) - (i < j);
+}
+int oracle_topk(const double *mass, int64_t rows, int64_t N, int64_t K, int32_t *idx) {
+  if (!mass || !idx || rows < 0 || N <= 0 || K < 0) return OR_ERR_ARG;
+  int64_t k = K < N ? K : N;
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+  if (!order) return OR_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t s = 0; s < N; ++s) order[s] = (int32_t)s;
+    topk_base = mass + r * N;   /* single-threaded: qsort has no context argument */
+    qsort(order, (size_t)N, sizeof(int32_t), topk_cmp);
+    qsort(order, (size_t)k, sizeof(int32_t), asc_cmp);
+    memcpy(idx + r * k, order, sizeof(int32_t) * (size_t)k);
+  }
+  free(order);
+  return OR_OK;
 }
