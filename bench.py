@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-token-sets", action="store_true", help="skip the token-level set measurements")
+    ap.add_argument("--no-selection", action="store_true", help="skip the exact-selection (anchor step) measurements")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip every measurement beside the headline step (CRM lists, sampler, token sets), "
                          "so that a profile holds only the headline kernel's launches")
@@ -49,6 +50,9 @@ def parse():
                     help="instead of the step: launch the attention kernel this many times on dense "
                          "1x40x16384 heads (every 128x128 block listed), print the median, and exit "
                          "(a short, fixed program for counter passes)")
+    ap.add_argument("--selection-only", action="store_true",
+                    help="instead of the step: run only the exact-selection (anchor step) measurements, "
+                         "print them as one JSON line, and exit")
     ap.add_argument("--n-xcd", type=int, default=8)
     ap.add_argument("--wave-rows", type=int, default=0)
     return ap.parse_args()
@@ -103,6 +107,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.dense_launches:
         dense_launches(torch, args.dense_launches)
+        return
+    if args.selection_only:
+        print(json.dumps({"exact_selection": selection_stage(torch)}), flush=True)
         return
 
     t0 = time.time()
@@ -165,6 +172,8 @@ def main():
     # token-level computational query sets (INTRA Scatter / Gather 0,
     # MC-Sparse-shaped token selection) on their own synthetic inputs
     token_sets = None if (args.no_token_sets or args.headline_only) else token_set_stage(torch)
+    # MC-Sparse's anchor step: dense pass, exact selection, sparse attention
+    selection = None if (args.no_selection or args.headline_only) else selection_stage(torch)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
@@ -213,6 +222,7 @@ def main():
         "crm_lists": crm,
         "importance_sampler": sampled,
         "token_sets": token_sets,
+        "exact_selection": selection,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config),
@@ -437,6 +447,71 @@ def token_set_stage(torch):
     timed("token_select_wan14b_15pct", "1x40 x 75600, d128, 128-query groups, 11340 keys each",
           *qkv(heads, heads, N), q_idx, kv_ptr, kv_idx, False, heads * N * K)
     del kv_idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def selection_stage(torch):
+    """MC-Sparse's anchor step (Algorithm 1) at Wan2.1-14B 720p: the dense
+    pass with log-sum-exp, exact selection (group mass, then top-K at 15 %
+    density) and token-level sparse attention on the selected keys; median of
+    5 launches of each after 2 warm-up rounds.  Groups are 128 consecutive
+    tokens of the (grouped) sequence; Q, K, V ~ N(0, 1) in bf16."""
+    from block_sparse_attention_mask_amd import api
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev).manual_seed(2025)
+    N, H, BQ, d = 75600, 40, 128, 128
+    K = int(0.15 * N)
+    C = -(-N // BQ)
+    f = lambda: torch.randn((1, H, N, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q, k, v = f(), f(), f()
+    q_idx = torch.arange(C * BQ, device=dev, dtype=torch.int32).reshape(1, C, BQ)
+    q_idx = torch.where(q_idx < N, q_idx, torch.full_like(q_idx, -1)).expand(H, C, BQ).contiguous()
+    nQB = -(-N // 128)
+    mask = torch.ones((H * nQB, nQB), dtype=torch.uint8, device=dev)
+    row_ptr, col, _ = api.build_csr(mask=mask, nQB=nQB)
+    del mask
+    o_full = torch.empty_like(q)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    mass = torch.empty((H * C, N), dtype=torch.float32, device=dev)
+    sel = torch.empty((H * C, K), dtype=torch.int32, device=dev)
+    kv_ptr = (torch.arange(H * C + 1, device=dev, dtype=torch.int64) * K).to(torch.int32)
+    o_sparse = torch.zeros_like(q)
+    steps = {
+        "dense_lse": lambda: api.attn_fwd(q, k, v, row_ptr, col, 128, out=o_full, lse=lse),
+        "group_mass": lambda: api.group_mass(q, k, lse, q_idx, out=mass),
+        "topk": lambda: api.topk_rows(mass, K, out=sel),
+        "sparse_attn": lambda: api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, sel.view(-1), out=o_sparse),
+    }
+    for _ in range(2):
+        for fn in steps.values():
+            fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ms = {}
+    for name, fn in steps.items():
+        t = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            fn()
+            b.record(s)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        ms[name] = float(np.median(t))
+    pairs = H * N * N
+    res = {
+        "shape": "1x40 x 75600, d128, 128-query groups, K = 11340 (15 %)",
+        "ms": {n_: round(t, 4) for n_, t in ms.items()},
+        "anchor_ms": round(sum(ms.values()), 4),
+        "dense_tflops": round(4.0 * d * pairs / (ms["dense_lse"] * 1e-3) / 1e12, 2),
+        "mass_tflops": round(2.0 * d * pairs / (ms["group_mass"] * 1e-3) / 1e12, 2),
+        "mass_flop_note": "2*d FLOP per (query, key) pair: the score product; one exp per pair on top",
+        "topk_gbps": round(H * C * N * 4 / (ms["topk"] * 1e-3) / 1e9, 1),
+        "sparse_tflops": round(4.0 * d * H * N * K / (ms["sparse_attn"] * 1e-3) / 1e12, 2),
+    }
+    log("exact selection: %s" % res)
+    del q, k, v, o_full, lse, mass, sel, o_sparse, row_ptr, col
     torch.cuda.empty_cache()
     return res
 

@@ -23,7 +23,7 @@ BSA_V_DIM_MAJOR = 1
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_crm_build", "bsa_crm_row_ptr",
            "bsa_crm_to_csr", "bsa_segment_offsets", "bsa_segment_means", "bsa_is_sample", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
-           "bsa_attn_fwd", "bsa_attn_tok_fwd",
+           "bsa_attn_fwd", "bsa_attn_tok_fwd", "bsa_group_mass", "bsa_topk_rows",
            "bsa_device_cus", "bsa_device_clock_khz", "bsa_clock_probe")
 
 
@@ -52,6 +52,20 @@ class TokArgs(ctypes.Structure):
         ("q_str", I64x3), ("k_str", I64x3), ("v_str", I64x3), ("o_str", I64x3),
         ("n_sets", I32), ("set_size", I32),
         ("q_idx", P), ("kv_ptr", P), ("kv_idx", P),
+        ("scale", ctypes.c_float),
+        ("causal", I32),
+    ]
+
+
+class MassArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", P), ("k", P), ("lse", P), ("mass", P),
+        ("B", I32), ("Hq", I32), ("Hkv", I32), ("d", I32),
+        ("N", I64),
+        ("q_str", I64x3), ("k_str", I64x3),
+        ("n_sets", I32), ("set_size", I32),
+        ("q_idx", P),
+        ("k0", I64), ("k1", I64),
         ("scale", ctypes.c_float),
         ("causal", I32),
     ]
@@ -115,6 +129,10 @@ def load():
         L.bsa_clock_probe.argtypes = [I32, I32, P, P]
         L.bsa_attn_tok_fwd.restype = ctypes.c_int
         L.bsa_attn_tok_fwd.argtypes = [ctypes.POINTER(TokArgs), P]
+        L.bsa_group_mass.restype = ctypes.c_int
+        L.bsa_group_mass.argtypes = [ctypes.POINTER(MassArgs), P]
+        L.bsa_topk_rows.restype = ctypes.c_int
+        L.bsa_topk_rows.argtypes = [P, I64, I64, I64, I32, P, P]
         L.bsa_device_cus.restype = ctypes.c_int
         L.bsa_device_cus.argtypes = []
         L.bsa_device_clock_khz.restype = ctypes.c_int

@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import AttnArgs, I64, I64x3, TokArgs, check, load
+from ._lib import AttnArgs, I64, I64x3, MassArgs, TokArgs, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
            "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus", "crm_build",
@@ -407,3 +407,59 @@ def attn_tok_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch
     a.causal = int(bool(causal))
     check("bsa_attn_tok_fwd", load().bsa_attn_tok_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def group_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, q_idx: torch.Tensor, keys=None,
+               out: Optional[torch.Tensor] = None, scale: float = 0.0, causal: bool = False, stream=None):
+    """Exact KV selection, mass pass: for each query set (q_idx int32
+    [B*Hq][n_sets][set_size]) and key s in keys = (k0, k1) (default all), the
+    sum over the set's queries of exp(q_t . k_s * scale - lse_t), lse float32
+    [B*Hq][N] from the dense pass.  Returns float32 [B*Hq*n_sets][k1 - k0]."""
+    for t, n in ((q, "q"), (k, "k")):
+        _dev(t, n, _BF16_LIKE)
+    _dev(lse, "lse", torch.float32)
+    _dev(q_idx, "q_idx", torch.int32)
+    if not lse.is_contiguous() or not q_idx.is_contiguous():
+        raise ValueError("lse and q_idx must be contiguous")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if q_idx.dim() != 3 or q_idx.shape[0] != B * Hq:
+        raise ValueError("q_idx must be [B*Hq][n_sets][set_size]")
+    if lse.shape != (B * Hq, N):
+        raise ValueError("lse must be [B*Hq][N]")
+    n_sets, set_size = q_idx.shape[1], q_idx.shape[2]
+    k0, k1 = (0, N) if keys is None else keys
+    shape = (B * Hq * n_sets, k1 - k0)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 %s" % (shape,))
+    a = MassArgs()
+    a.q, a.k, a.lse, a.mass = _ptr(q), _ptr(k), _ptr(lse), _ptr(out)
+    a.B, a.Hq, a.Hkv, a.d, a.N = B, Hq, Hkv, d, N
+    a.q_str, a.k_str = _strides(q), _strides(k)
+    a.n_sets, a.set_size = n_sets, set_size
+    a.q_idx = _ptr(q_idx)
+    a.k0, a.k1 = int(k0), int(k1)
+    a.scale = float(scale)
+    a.causal = int(bool(causal))
+    check("bsa_group_mass", load().bsa_group_mass(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def topk_rows(x: torch.Tensor, k: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Column indices of the k largest values of each row of x (float32
+    [rows][n], unit column stride), ties to the lower index, ascending:
+    int32 [rows][min(k, n)]."""
+    _dev(x, "x", torch.float32)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [rows][n] with unit column stride")
+    rows, n = x.shape
+    kk = min(int(k), n)
+    if out is None:
+        out = torch.empty((rows, kk), dtype=torch.int32, device=x.device)
+    elif out.dtype != torch.int32 or tuple(out.shape) != (rows, kk) or not out.is_contiguous():
+        raise ValueError("out must be contiguous int32 [rows][min(k, n)]")
+    check("bsa_topk_rows", load().bsa_topk_rows(_ptr(x), rows, n, x.stride(0), int(k), _ptr(out),
+                                                _stream(stream)))
+    return out

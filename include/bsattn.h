@@ -412,6 +412,66 @@ typedef struct {
 int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Exact token-level KV selection, mass pass.
+ *
+ * Source: MC-Sparse, "The MC-Sparse Architecture" and Algorithm 1 (at an
+ * anchor step, dense FlashAttention returns each query's log-sum-exp l_t;
+ * exact KV selection then ranks, for every query group, the keys by the
+ * attention probability mass the group's queries place on them).  For every
+ * set c (a query group) and key s in [k0, k1):
+ *   mass[c][s - k0] = sum over the set's queries t of exp(q_t . k_s * scale - l_t)
+ * where l_t = lse[bh][t] (natural log, as bsa_attn_fwd writes it) and, when
+ * causal, keys s > t add nothing for query t (lse must then come from a
+ * causal pass).  Empty slots, and queries whose lse is -inf or NaN, add
+ * nothing.
+ *
+ * q [B][Hq][N][d], k [B][Hkv][N][d]: bf16 (uint16 bits) token-major device
+ * tensors addressed by the strides (d contiguous, 16-byte aligned bases,
+ * strides multiples of 8; per-head byte extents below 2^30); query head h
+ * reads KV head h / (Hq / Hkv).  lse: device float32 [B*Hq][N], contiguous.
+ * q_idx: device int32 [B*Hq][n_sets][set_size] query positions, a position
+ * outside [0, N) being an empty slot.  mass: device float32
+ * [B*Hq*n_sets][k1 - k0], contiguous, fully written.  d must be 128 and
+ * set_size 64 or 128 (BSA_ERR_UNSUPPORTED otherwise, and for larger
+ * extents); BSA_ERR_ARG for NULL pointers, non-positive sizes, Hq % Hkv != 0,
+ * misaligned strides or 0 <= k0 <= k1 <= N violated.  scale <= 0 selects
+ * 1/sqrt(d).  The summation order is fixed: results are deterministic.
+ * Asynchronous.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k;
+  const float *lse;
+  float *mass;
+  int32_t B, Hq, Hkv, d;
+  int64_t N;
+  int64_t q_str[3], k_str[3];
+  int32_t n_sets, set_size;
+  const int32_t *q_idx;
+  int64_t k0, k1; /* key range of the output columns */
+  float scale;
+  int32_t causal;
+} bsa_mass_args;
+
+int bsa_group_mass(const bsa_mass_args *a, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Exact token-level KV selection, top-K pass.
+ *
+ * Source: MC-Sparse, "The MC-Sparse Architecture" (each query group keeps the
+ * K keys of largest attention mass: rank by score, take the top K, gather
+ * their key and value vectors).  For each row r of x (device float32,
+ * row stride ld >= n elements), idx[r][0 .. kk) (device int32, contiguous,
+ * kk = min(k, n)) receives the column indices of the kk largest values in
+ * ascending index order; among equal values the lower index is taken first
+ * (-0 and +0 count as equal; NaN values must not occur).  kk = n lists every
+ * column.  Nothing is enqueued for rows = 0 or k = 0.  BSA_ERR_ARG for NULL
+ * pointers, n <= 0, ld < n, rows < 0 or k < 0; BSA_ERR_UNSUPPORTED for
+ * n > 77824.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_topk_rows(const float *x, int64_t rows, int64_t n, int64_t ld, int32_t k, int32_t *idx,
+                  bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Engine-clock probe under MFMA load (for reading a measurement against the
  * clock the device sustains, not the path itself).  Launches `blocks`
  * workgroups of four wavefronts; each wavefront runs `iters` iterations of

@@ -177,6 +177,56 @@ def test_attn_tok_argument_errors(L, kw, code):
     assert L.bsa_attn_tok_fwd(None, None) == _lib.BSA_ERR_ARG
 
 
+def _mass_args(**kw):
+    a = _lib.MassArgs()
+    a.q, a.k, a.lse, a.mass = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
+    a.B, a.Hq, a.Hkv, a.d, a.N = 1, 4, 2, 128, 1000
+    a.q_str = a.k_str = _lib.I64x3(4 * 1000 * 128, 1000 * 128, 128)
+    a.n_sets, a.set_size = 4, 128
+    a.q_idx = FAKE
+    a.k0, a.k1 = 0, 1000
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.BSA_ERR_ARG),
+    (dict(lse=None), _lib.BSA_ERR_ARG),
+    (dict(mass=None), _lib.BSA_ERR_ARG),
+    (dict(q_idx=None), _lib.BSA_ERR_ARG),
+    (dict(d=64), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(set_size=32), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(Hq=3), _lib.BSA_ERR_ARG),
+    (dict(N=0), _lib.BSA_ERR_ARG),
+    (dict(k0=-1), _lib.BSA_ERR_ARG),
+    (dict(k1=1001), _lib.BSA_ERR_ARG),
+    (dict(k0=600, k1=500), _lib.BSA_ERR_ARG),
+    (dict(q=ctypes.c_void_p(4104)), _lib.BSA_ERR_ARG),
+    (dict(k_str=_lib.I64x3(4 * 1000 * 128, 1000 * 128, 130)), _lib.BSA_ERR_ARG),
+    (dict(N=1 << 23, k1=1 << 23), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(k0=500, k1=500), _lib.BSA_OK),       # empty key range: nothing enqueued
+    (dict(n_sets=0), _lib.BSA_OK),             # no set: nothing enqueued
+])
+def test_group_mass_argument_errors(L, kw, code):
+    a = _mass_args(**kw)
+    assert L.bsa_group_mass(ctypes.byref(a), None) == code
+    assert L.bsa_group_mass(None, None) == _lib.BSA_ERR_ARG
+
+
+def test_topk_rows_argument_errors(L):
+    f = L.bsa_topk_rows
+    assert f(None, 4, 100, 100, 10, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, 4, 100, 100, 10, None, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, -1, 100, 100, 10, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, 4, 0, 100, 10, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, 4, 100, 99, 10, FAKE, None) == _lib.BSA_ERR_ARG     # ld < n
+    assert f(FAKE, 4, 100, 100, -1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, 4, 77825, 77825, 10, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert f(FAKE, 0, 100, 100, 10, FAKE, None) == _lib.BSA_OK          # nothing enqueued
+    assert f(FAKE, 4, 100, 100, 0, FAKE, None) == _lib.BSA_OK
+
+
 def _args(**kw):
     a = _lib.AttnArgs()
     a.q, a.k, a.v, a.o = FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(16384), ctypes.c_void_p(32768)
