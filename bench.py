@@ -452,8 +452,8 @@ def token_set_stage(torch):
 
 
 def selection_stage(torch):
-    """MC-Sparse's anchor step (Algorithm 1) at Wan2.1-14B 720p: the dense
-    pass with log-sum-exp, exact selection (group mass, then top-K at 15 %
+    """MC-Sparse's anchor step (Algorithm 1) at Wan2.1-14B 720p: V to the
+    dim-major layout, the dense pass with log-sum-exp, exact selection (group mass, then top-K at 15 %
     density) and token-level sparse attention on the selected keys; median of
     5 launches of each after 2 warm-up rounds.  Groups are 128 consecutive
     tokens of the (grouped) sequence; Q, K, V ~ N(0, 1) in bf16."""
@@ -472,13 +472,15 @@ def selection_stage(torch):
     row_ptr, col, _ = api.build_csr(mask=mask, nQB=nQB)
     del mask
     o_full = torch.empty_like(q)
+    vt = api.transpose_rows(v)
     lse = torch.empty((H, N), dtype=torch.float32, device=dev)
     mass = torch.empty((H * C, N), dtype=torch.float32, device=dev)
     sel = torch.empty((H * C, K), dtype=torch.int32, device=dev)
     kv_ptr = (torch.arange(H * C + 1, device=dev, dtype=torch.int64) * K).to(torch.int32)
     o_sparse = torch.zeros_like(q)
     steps = {
-        "dense_lse": lambda: api.attn_fwd(q, k, v, row_ptr, col, 128, out=o_full, lse=lse),
+        "v_transpose": lambda: api.transpose_rows(v, dst=vt),
+        "dense_lse": lambda: api.attn_fwd(q, k, vt, row_ptr, col, 128, out=o_full, lse=lse, v_dim_major=True),
         "group_mass": lambda: api.group_mass(q, k, lse, q_idx, out=mass),
         "topk": lambda: api.topk_rows(mass, K, out=sel),
         "sparse_attn": lambda: api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, sel.view(-1), out=o_sparse),
@@ -511,7 +513,7 @@ def selection_stage(torch):
         "sparse_tflops": round(4.0 * d * H * N * K / (ms["sparse_attn"] * 1e-3) / 1e12, 2),
     }
     log("exact selection: %s" % res)
-    del q, k, v, o_full, lse, mass, sel, o_sparse, row_ptr, col
+    del q, k, v, vt, o_full, lse, mass, sel, o_sparse, row_ptr, col
     torch.cuda.empty_cache()
     return res
 

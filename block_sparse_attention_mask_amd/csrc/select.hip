@@ -9,11 +9,14 @@
 //
 // group_mass -- one workgroup per (group, key chunk), eight wavefronts, two
 //   per SIMD.  Wavefront w owns half w % 2 of the group's queries and the key
-//   quarter w / 2 (32 keys) of every 128-key tile.  S = Q K^T runs on
-//   32x32x16 bf16 MFMA with the query fragments held in registers for the
-//   whole chunk (A operand, one query row per lane) and the key fragments
-//   loaded straight from HBM (B operand, one key column per lane), so a lane
-//   ends with 16 query rows of one key column: p = exp2(s * c - l2_t) is
+//   quarter w / 2 (32 keys) of every 128-key tile.  Key tiles stream through
+//   four LDS stages by LDS DMA (buffer_load ... lds, 16-byte chunks of each
+//   key row at XOR-swizzled positions), three tiles ahead, one barrier per
+//   tile; both query halves read the same staged tile.  The scores of the
+//   next tile are computed while the current tile's exponentials run.  S = Q K^T runs on 32x32x16 bf16 MFMA with the query fragments held
+//   in registers for the whole chunk (A operand, one query row per lane) and
+//   the key fragments read from LDS (B operand, one key column per lane), so
+//   a lane ends with 16 query rows of one key column: p = exp2(s * c - l2_t) is
 //   summed down the column in registers, the two lane halves are added with
 //   one cross-lane exchange, and the two query halves meet in LDS, flushed
 //   once per 1024 keys.  Summation order is fixed, so results are
@@ -27,6 +30,8 @@
 //   pair of workgroup scans over the counts of keys above it and equal to
 //   it places every selected index: all keys above the threshold and the
 //   lowest-indexed ties, written in ascending index order.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace bsa {
@@ -46,18 +51,21 @@ struct MassParams {
   float c;        // scale * log2(e)
 };
 
-constexpr int kSuper = 1024;   // keys per LDS flush (eight 128-key tiles)
+constexpr int kSuper = 1024;      // keys per LDS flush (eight 128-key tiles)
+constexpr int kStages = 4;        // K tiles staged in LDS
+constexpr int kTileBytes = 128 * 128 * 2;
 
 template <int BQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void group_mass(MassParams p) {
   constexpr int D = 128, KS = D / 16, QT = BQ / 64, HALF = BQ / 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[kStages][kTileBytes];
+  __shared__ float part[2][2][kSuper];   // [buffer][query half][key of the super tile]
   __shared__ int32_t qpos[BQ];
   __shared__ float ql2[BQ];
-  __shared__ float part[2][2][kSuper];   // [buffer][query half][key of the super tile]
   __shared__ int tlo, thi;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qh = wave & 1, kq = wave >> 1;
   const int ln = lane & 31, hf = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x % p.rows;
@@ -88,7 +96,7 @@ void group_mass(MassParams p) {
   float *mrow = p.mass + row * p.ldm - p.k0;
 
   const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((int64_t)(N - 1) * p.qs2 + D) * 2);
-  const rsrc_t krs = make_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
+  const i32x4 krs = buffer_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
 
   // Q fragments (A operand): lane (ln, hf) of tile qt holds query slot
   // HALF qh + 32 qt + ln, dims 16 ks + 8 hf .. +7
@@ -107,23 +115,51 @@ void group_mass(MassParams p) {
     for (int i = 0; i < 16; ++i) l2[qt][i] = ql2[HALF * qh + 32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3)];
   }
 
+  // K tiles: copy I (0..31) of a tile fills LDS bytes [1024 I, 1024 I + 1024),
+  // rows 4 I .. 4 I + 3; lane l writes row 4 I + l / 16 at chunk position
+  // l % 16, which holds source chunk (l % 16) ^ (row mod 16).  Wavefront w
+  // issues copies w, w + 8, w + 16, w + 24.  Keys at or past kc read zeros,
+  // and so do the copies issued for tiles past the end, which keeps every
+  // wavefront's count of copies in flight the same in every iteration.
   const uint32_t ks2b = (uint32_t)p.ks2 * 2;
-  auto load_k = [&](bf16x8 (&kf)[KS], int key) {
-    const bool ok = key < kc;
-    const uint32_t rb = ok ? (uint32_t)key * ks2b + hf * 16 : kOOR;
+  int crow[4];
+  uint32_t coff[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, ok ? rb + ks * 32 : kOOR, 0, 0));
+  for (int t = 0; t < 4; ++t) {
+    crow[t] = 4 * (wave + 8 * t) + (lane >> 4);
+    coff[t] = (uint32_t)crow[t] * ks2b + ((((uint32_t)lane & 15u) ^ ((uint32_t)crow[t] & 15u)) << 4);
+  }
+  auto lds_addr = [](const uint8_t *ptr) -> uint32_t {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)ptr;
+  };
+  auto issue = [&](int jt) {
+    const int tile0 = ka + 128 * jt;
+    const uint32_t dst = lds_addr(kt[jt & (kStages - 1)]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t off = tile0 + crow[t] < kc ? (uint32_t)tile0 * ks2b + coff[t] : kOOR;
+      lds_copy16(krs, dst + 1024u * (wave + 8 * t), off, 0u);
+    }
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto flush = [&](int sup) {
+    const int s0 = ka + kSuper * sup;
+    const int send = min(kc, s0 + kSuper);
+    for (int x = tid; x < send - s0; x += 512) mrow[s0 + x] = part[sup & 1][0][x] + part[sup & 1][1][x];
   };
 
   const int ntile = (kc - ka + 127) >> 7;
-  bf16x8 kf[KS], kn[KS];
-  if (ntile > 0) load_k(kf, ka + 32 * kq + ln);
-  for (int j = 0; j < ntile; ++j) {
-    const int tile0 = ka + 128 * j;
-    const int key = tile0 + 32 * kq + ln;
-    if (j + 1 < ntile) load_k(kn, key + 128);
-    f32x16 acc[QT];
+  const int r = 32 * kq + ln;   // this lane's key within a tile
+  auto scores = [&](f32x16 (&acc)[QT], int jt) {   // S of tile jt from its LDS stage
+    const uint8_t *kst = kt[jt & (kStages - 1)];
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8 *>(kst + r * 256 + (((2 * ks + hf) ^ (r & 15)) << 4));
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -133,34 +169,62 @@ void group_mass(MassParams p) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
         acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qt][ks], kf[ks], acc[qt], 0, 0, 0);
-    float col = 0.f;
-    if (p.causal && tile0 + 127 > tmin) {
+  };
+  // Software pipeline: the scores of tile j+1 are computed (MFMA) in the same
+  // basic block as the exponentials of tile j (VALU), so the two overlap
+  // within each wavefront.  Tile j+4 is copied into the stage of tile j once
+  // the barrier shows every wavefront has read it.
+  f32x16 acc[QT], accn[QT];
+#pragma unroll
+  for (int jt = 0; jt < kStages; ++jt) issue(jt);
+  if (ntile > 0) {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0_wait_imm(4 * (kStages - 1)));
+    barrier();
+    scores(acc, 0);
+  }
+  for (int j = 0; j < ntile; ++j) {
+    // tile j+1 has landed once at most the copies of tiles j+2, j+3 are in
+    // flight; the barrier also marks the stage of tile j as read by all
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0_wait_imm(4 * (kStages - 2)));
+    barrier();
+    if (j > 0 && (j & 7) == 0) flush((j >> 3) - 1);
+    issue(j + kStages);
+    const int tile0 = ka + 128 * j;
+    const int key = tile0 + r;
+    auto step = [&](auto masked) {
+      scores(accn, j + 1);   // past the end: a stage of zeros, result unused
+      float col = 0.f;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int t = qpos[HALF * qh + 32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3)];
-          const float x = key > t ? -INFINITY : fmaf(acc[qt][i], p.c, -l2[qt][i]);
+          float x = fmaf(acc[qt][i], p.c, -l2[qt][i]);
+          if (decltype(masked)::value) {
+            const int t = qpos[HALF * qh + 32 * qt + 8 * (i >> 2) + 4 * hf + (i & 3)];
+            x = key > t ? -INFINITY : x;
+          }
           col += __builtin_amdgcn_exp2f(x);
         }
-    } else {
+      col += __shfl_xor(col, 32, 64);
+      if (hf == 0) part[(j >> 3) & 1][qh][128 * (j & 7) + r] = col;
+      if (!decltype(masked)::value) {
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // SGB: the K fragment reads
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+        for (int m = 0; m < QT * KS; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // SGB: one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // SGB: six VALU
+        }
+      }
+    };
+    if (p.causal && tile0 + 127 > tmin) step(std::integral_constant<bool, true>());
+    else step(std::integral_constant<bool, false>());
 #pragma unroll
-        for (int i = 0; i < 16; ++i) col += __builtin_amdgcn_exp2f(fmaf(acc[qt][i], p.c, -l2[qt][i]));
-    }
-    col += __shfl_xor(col, 32, 64);
-    const int buf = (j >> 3) & 1;
-    if (hf == 0) part[buf][qh][128 * (j & 7) + 32 * kq + ln] = col;
-    if ((j & 7) == 7 || j + 1 == ntile) {
-      __syncthreads();
-      const int s0 = ka + kSuper * (j >> 3);
-      const int send = min(kc, s0 + kSuper);
-      for (int x = tid; x < send - s0; x += 512) mrow[s0 + x] = part[buf][0][x] + part[buf][1][x];
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
+    for (int qt = 0; qt < QT; ++qt) acc[qt] = accn[qt];
   }
+  // every copy (the ones past the end too) lands before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier();
+  if (ntile > 0) flush((ntile - 1) >> 3);
   // keys past the group's last query (causal) carry no mass
   for (int x = kc + tid; x < kb; x += 512) mrow[x] = 0.f;
 }
@@ -279,7 +343,9 @@ extern "C" int bsa_group_mass(const bsa_mass_args *a, bsa_stream_t stream) {
   const int64_t rows = (int64_t)a->B * a->Hq * a->n_sets;
   const int64_t W = a->k1 - a->k0;
   if (rows == 0 || W == 0) return BSA_OK;
-  // split a row's key range so that a launch holds enough workgroups
+  // Split a row's key range only when a launch would otherwise hold too few
+  // workgroups (K is re-read per group either way; splitting further only
+  // adds per-workgroup set-up).
   const int64_t want = 4096;
   int64_t nsplit = (want + rows - 1) / rows;
   const int64_t max_split = (W + kSuper - 1) / kSuper;
