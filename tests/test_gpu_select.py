@@ -192,3 +192,58 @@ def test_wan14b_720p_sampled():
         ref = oracle.group_mass(q[:, h:h + 1], k[:, h:h + 1], q_idx[h:h + 1, c:c + 1])
         _check_mass(gm[r:r + 1], ref, "head %d group %d" % (h, c))
         _near_tie_check(gs[r:r + 1], oracle.topk(ref, K), ref, K)
+
+
+def test_llama3_8b_32k_causal_sampled():
+    """Causal selection with GQA at the LLaMA-3.1-8B prefill shape (32 query
+    heads over 8 KV heads, 32,768 tokens, groups of 128 consecutive tokens,
+    K = 4096): every launch at full size, sampled groups against the oracle.
+    The first group has mass on its first 128 keys only, so most of its
+    selection is the lowest-indexed zero-mass keys."""
+    B, Hq, Hkv, N, BQ, K = 1, 32, 8, 32768, 128, 4096
+    q, k, v = _qkv(32, B, Hq, Hkv, N)
+    C = N // BQ
+    q_idx = np.broadcast_to(np.arange(N, dtype=np.int32).reshape(1, C, BQ), (B * Hq, C, BQ)).copy()
+    qd, kd, vd = (_gpu(a.view(np.int16)) for a in (q, k, v))
+    _log("llama 32k: dense causal pass")
+    _, lse = _dense_lse(qd, kd, vd, True)
+    _log("llama 32k: mass + top-K")
+    mass = api.group_mass(qd, kd, lse, _gpu(q_idx), causal=True)
+    sel = api.topk_rows(mass, K)
+    torch.cuda.synchronize()
+    picks = [(0, 0), (13, 100), (31, C - 1)]
+    rows = [h * C + c for h, c in picks]
+    gm = mass[rows].cpu().numpy()
+    gs = sel[rows].cpu().numpy()
+    np.testing.assert_array_equal(gs, oracle.topk(gm, K))
+    for r, (h, c) in enumerate(picks):
+        g = h // (Hq // Hkv)
+        _log("  oracle head %d (kv %d) group %d" % (h, g, c))
+        ref = oracle.group_mass(q[:, h:h + 1], k[:, g:g + 1], q_idx[h:h + 1, c:c + 1], causal=True)
+        assert np.all(gm[r, (c + 1) * BQ:] == 0) and np.all(ref[0, (c + 1) * BQ:] == 0)
+        _check_mass(gm[r:r + 1], ref, "head %d group %d" % (h, c))
+        _near_tie_check(gs[r:r + 1], oracle.topk(ref, K), ref, K)
+
+
+def test_dead_queries_add_nothing():
+    """A query whose log-sum-exp is -inf or NaN adds nothing: the masses equal,
+    bit for bit, those of the same sets with that query's slot emptied (the
+    summation order is fixed)."""
+    B, Hq, Hkv, N, BQ = 1, 2, 2, 700, 128
+    q, k, v = _qkv(91, B, Hq, Hkv, N)
+    q_idx = _groups(92, B * Hq, N, BQ)
+    qd, kd, vd = (_gpu(a.view(np.int16)) for a in (q, k, v))
+    _, lse = _dense_lse(qd, kd, vd, False)
+    dead = q_idx.copy()
+    lse_dead = lse.clone()
+    g = np.random.default_rng(93)
+    for h in range(B * Hq):
+        pos = g.choice(N, size=40, replace=False)
+        lse_dead[h, pos[:20]] = float("-inf")
+        lse_dead[h, pos[20:]] = float("nan")
+        dead[h][np.isin(dead[h], pos)] = -1
+    for causal in (False, True):
+        a = api.group_mass(qd, kd, lse_dead, _gpu(q_idx), causal=causal)
+        b = api.group_mass(qd, kd, lse, _gpu(dead), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), causal
