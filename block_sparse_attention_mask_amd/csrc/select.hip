@@ -245,7 +245,7 @@ constexpr int kTopkLong = 152;
 
 template <int E, int NT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT)))
-void topk_rows(const float *x, int64_t ld, int n, int k, int32_t *idx) {
+void topk_rows(const float *x, int64_t ld, int n, int k, int32_t *idx, int vec) {
   constexpr int NWV = NT / 64;
   __shared__ int red[2][NWV];
   __shared__ int scan_gt[NWV], scan_eq[NWV];
@@ -255,10 +255,26 @@ void topk_rows(const float *x, int64_t ld, int n, int k, int32_t *idx) {
   int32_t *out = idx + row * (int64_t)k;
   const int base = tid * E;
 
-  // padding keys are 0, below every candidate, so they are never counted
+  // padding keys are 0, below every candidate, so they are never counted.
+  // With 16-byte aligned rows each lane loads four keys at a time.
   uint32_t key[E];
+  if (vec) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(xr[base + e]) : 0u;
+    for (int e = 0; e < E; e += 4) {
+      const int i = base + e;
+      if (i + 3 < n) {
+        const float4 v = *reinterpret_cast<const float4 *>(xr + i);
+        key[e] = order_key(v.x); key[e + 1] = order_key(v.y);
+        key[e + 2] = order_key(v.z); key[e + 3] = order_key(v.w);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[e + u] = i + u < n ? order_key(xr[i + u]) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = base + e < n ? order_key(xr[base + e]) : 0u;
+  }
 
   // threshold T: the largest key with at least k keys >= T
   uint32_t T = 0;
@@ -391,13 +407,15 @@ extern "C" int bsa_topk_rows(const float *x, int64_t rows, int64_t n, int64_t ld
   if (rows >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   const int kk = k < n ? k : (int)n;
   const int nn = (int)n;
+  // every row start 16-byte aligned: four-key loads (E is a multiple of 4)
+  const int vec = (ld % 4 == 0 && bsa_aligned16(x)) ? 1 : 0;
   hipStream_t s = bsa_hip_stream(stream);
   const dim3 grid((unsigned)rows);
-  if (n <= 4 * 1024) hipLaunchKernelGGL((topk_rows<4, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx);
-  else if (n <= 8 * 1024) hipLaunchKernelGGL((topk_rows<8, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx);
-  else if (n <= 16 * 1024) hipLaunchKernelGGL((topk_rows<16, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx);
-  else if (n <= 32 * 1024) hipLaunchKernelGGL((topk_rows<32, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx);
-  else hipLaunchKernelGGL((topk_rows<kTopkLong, 512>), grid, dim3(512), 0, s, x, ld, nn, kk, idx);
+  if (n <= 4 * 1024) hipLaunchKernelGGL((topk_rows<4, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx, vec);
+  else if (n <= 8 * 1024) hipLaunchKernelGGL((topk_rows<8, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx, vec);
+  else if (n <= 16 * 1024) hipLaunchKernelGGL((topk_rows<16, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx, vec);
+  else if (n <= 32 * 1024) hipLaunchKernelGGL((topk_rows<32, 1024>), grid, dim3(1024), 0, s, x, ld, nn, kk, idx, vec);
+  else hipLaunchKernelGGL((topk_rows<kTopkLong, 512>), grid, dim3(512), 0, s, x, ld, nn, kk, idx, vec);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }
