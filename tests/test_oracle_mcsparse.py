@@ -7,6 +7,8 @@ the top-K keys by that mass).
 * closed form: every query's probabilities sum to 1, so a group's masses sum
   to its number of valid queries (empty slots add nothing);
 * causal: no mass after the group's last query;
+* closed form: with every key equal, each probability is 1/N (causal:
+  1/(t+1) on the keys up to t);
 * a restricted key range is the slice of the full result;
 * top-K: numpy's lexsort by (mass descending, index ascending), with planted
   ties, K >= N and K = 0.
@@ -110,3 +112,25 @@ def test_topk_matches_lexsort_with_ties(K):
     assert got.shape == (rows, min(K, N))
     if K > 0:
         assert np.all(np.diff(got, axis=1) > 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_group_mass_closed_form_equal_keys(causal):
+    """Every key the same vector: each query's scores are all equal, so its
+    probabilities are 1/N (causal: 1/(t+1) on keys s <= t) and a key's mass is
+    the sum of those over the group's queries."""
+    B, Hq, Hkv, N, d, C, BQ = 1, 2, 1, 97, 16, 4, 8
+    g = np.random.default_rng(14)
+    q = synth.f32_to_bf16_bits(g.standard_normal((B, Hq, N, d)).astype(np.float32))
+    row = synth.f32_to_bf16_bits(g.standard_normal(d).astype(np.float32))
+    k = np.broadcast_to(row, (B, Hkv, N, d)).copy()
+    q_idx = g.integers(-3, N, size=(B * Hq, C, BQ)).astype(np.int32)
+    got = oracle.group_mass(q, k, q_idx, causal=causal)
+    want = np.zeros_like(got)
+    for r, ts in enumerate(q_idx.reshape(-1, BQ)):
+        for t in ts[(ts >= 0) & (ts < N)]:
+            if causal:
+                want[r, :t + 1] += 1.0 / (t + 1)
+            else:
+                want[r] += 1.0 / N
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
