@@ -279,8 +279,32 @@ void topk_rows(const float *x, int64_t ld, int n, int k, int32_t *idx, int vec) 
   // threshold T: the largest key with at least k keys >= T
   uint32_t T = 0;
   if (k < n) {
+    // Bits above the highest one in which the row's keys differ are the same
+    // in every key (padding keys, 0, left out): a candidate with such a bit
+    // counts all n keys or none, so T takes them as they are and the search
+    // starts below them.
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e]) { lo = min(lo, key[e]); hi = max(hi, key[e]); }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+    }
+    if (lane == 0) { red[0][wave] = (int)lo; red[1][wave] = (int)hi; }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      lo = min(lo, (uint32_t)red[0][w]);
+      hi = max(hi, (uint32_t)red[1][w]);
+    }
+    __syncthreads();   // red is reused by the counting passes
+    const uint32_t diff = lo ^ hi;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
+    T = top < 0 ? hi : (top >= 31 ? 0u : hi & ~((2u << top) - 1u));
     int it = 0;
-    for (int bit = 31; bit >= 0; --bit, ++it) {
+    for (int bit = top; bit >= 0; --bit, ++it) {
       const uint32_t cand = T | (1u << bit);
       int c = 0;
 #pragma unroll
