@@ -147,11 +147,12 @@ def _near_tie_check(sel, ref_sel, ref_mass, K):
         assert np.all(np.abs(ref_mass[r, diff] - kth) <= band), (r, diff[:8], ref_mass[r, diff[:8]], kth)
 
 
+@pytest.mark.parametrize("BQ", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_selection_end_to_end(causal):
-    B, Hq, Hkv, N, BQ, K = 1, 2, 1, 2000, 128, 300
+def test_selection_end_to_end(causal, BQ):
+    B, Hq, Hkv, N, K = 1, 2, 1, 2000, 300                   # few groups: the key range is split
     q, k, v = _qkv(40 + causal, B, Hq, Hkv, N, scale_q=2.0)
-    q_idx = _groups(41, B * Hq, N, BQ)
+    q_idx = _groups(41 + BQ, B * Hq, N, BQ)
     qd, kd, vd = (_gpu(a.view(np.int16)) for a in (q, k, v))
     _, lse = _dense_lse(qd, kd, vd, causal)
     mass = api.group_mass(qd, kd, lse, _gpu(q_idx), causal=causal)
