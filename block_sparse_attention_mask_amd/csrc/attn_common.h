@@ -1,5 +1,7 @@
 // Internal: parameters and helpers shared by the attention kernels.
 #pragma once
+#include <type_traits>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -96,7 +98,26 @@ __device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t lds, uint32_t vo
                "s"(rsrc), "s"(soff)
                : "m0");
 }
+
+// The same copy with the LDS address formed in the instruction stream: M0 =
+// base + IMM, so that a kernel keeps one SGPR of LDS base per wavefront
+// instead of one per (buffer, copy slot).
+template <uint32_t IMM>
+__device__ __forceinline__ void lds_copy16_at(i32x4 rsrc, uint32_t base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(base), "v"(voff),
+               "s"(rsrc), "s"(soff), "n"(IMM)
+               : "m0", "scc");
+}
 #pragma clang diagnostic pop
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    static_for<B + 1, E>(f);
+  }
+}
 
 // s_waitcnt immediate (gfx9 encoding): at most n vector-memory operations of
 // this wavefront outstanding, no LDS/scalar-memory operation outstanding,

@@ -70,13 +70,13 @@ struct PCfg {
   static constexpr int VC = HK / 8;                 // 16-byte chunks per V^T half row
   static constexpr int NKC = HK * KC / 64;          // 1 KB copies per K half tile
   static constexpr int NVC = D * VC / 64;           // 1 KB copies per V^T half tile
-  static constexpr int NSK = NKC / NW, NSV = NVC / NW;
-  static constexpr int NSLOT = NSK + NSV;           // copies per wavefront per phase
+  // the four softmax-step wavefronts of a phase issue all of its copies
+  static constexpr int NSK = NKC / NQG, NSV = NVC / NQG;
+  static constexpr int NSLOT = NSK + NSV;           // copies per softmax step
   static constexpr int KB = NKC * 1024, VB = NVC * 1024;
   static constexpr int NM = MTW * (2 * DT + KS);    // MFMAs per matrix step
   static constexpr int LIST = 1024;                 // CSR entries staged in LDS at a time
-  static_assert(NKC % NW == 0 && NVC % NW == 0, "whole copies per wavefront");
-  static_assert(NM % NSLOT == 0, "copies spread evenly over the matrix step");
+  static_assert(NKC % NQG == 0 && NVC % NQG == 0, "whole copies per wavefront");
   static_assert((2 * MTW) % NSLOT == 0 || NSLOT % (2 * MTW) == 0, "copies spread evenly over the softmax step");
   static_assert(64 * DT * 16 * 4 <= KB, "merge data of a query group fits a K buffer");
 };
@@ -88,11 +88,16 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
                                              const int32_t *__restrict__ sperm, uint16_t *__restrict__ out,
                                              float *__restrict__ lse) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t kx0[C::KB], kx1[C::KB], ky0[C::KB], ky1[C::KB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vx0[C::VB], vx1[C::VB], vy0[C::VB], vy1[C::VB];
+  // LDS: K buffers 0-3 (kx0, kx1, ky0, ky1), V^T buffers 4-7 (vx0, vx1, vy0,
+  // vy1), each C::KB bytes; buffer i starts at byte i * C::KB of smem.
+  static_assert(C::KB == C::VB, "K and V^T half tiles have the same size");
+  constexpr int KX0 = 0, KX1 = 1, KY0 = 2, KY1 = 3, VX0 = 4, VX1 = 5, VY0 = 6, VY1 = 7;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[8 * C::KB];
   __shared__ int32_t lcol[C::LIST];
   __shared__ float lbias[C::LIST];
-  __shared__ float mrg_ml[C::NQG][2][64];
+  // per key half and query group: l, cold-tile max, overflow flag, running max
+  __shared__ float mrg[2][4][C::NQG][64];
+  __shared__ int redo_vote[C::NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,16 +150,16 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
   }
 
-  // Copy slots.  Slot t of wavefront w is copy c = w + 8 t of a phase: K copy
-  // c for t < NSK, else V^T copy c - NKC.  Copy c writes LDS bytes
-  // [1024 c, 1024 c + 1024) of its buffer; lane l writes LDS slot 64 c + l,
-  // which holds (row, chunk position) = divmod(slot, row chunks), so the lane
-  // reads source chunk position ^ swz(row).  lo[t] is that source offset
-  // within the half tile.
+  // Copy slots.  Slot t of the wavefront of query group qg is copy
+  // c = qg + 4 t of a pair of half tiles: K copy c for t < NSK, else V^T copy
+  // c - NKC.  Copy c writes LDS bytes [1024 c, 1024 c + 1024) of its buffer;
+  // lane l writes LDS slot 64 c + l, which holds (row, chunk position) =
+  // divmod(slot, row chunks), so the lane reads source chunk position ^
+  // swz(row).  lo[t] is that source offset within the half tile.
   uint32_t lo[C::NSLOT];
 #pragma unroll
   for (int t = 0; t < C::NSLOT; ++t) {
-    const int c = wave + C::NW * t;
+    const int c = qg + C::NQG * t;
     if (t < C::NSK) {
       const int s = c * 64 + lane, row = s / C::KC, ch = (s % C::KC) ^ swz<C::KC>(row);
       lo[t] = (uint32_t)row * ks2b + ch * 16;
@@ -163,9 +168,10 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
       lo[t] = (uint32_t)row * vs2b + ch * 16;
     }
   }
-  auto lds_addr = [](const uint8_t *ptr) -> uint32_t {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)ptr;
-  };
+  // LDS address of this wavefront's first copy destination (buffer 0, copy
+  // c = qg); every copy's M0 is this plus a compile-time offset
+  const uint32_t wbase =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)smem + (uint32_t)qg * 1024u;
 
   int n = 0;   // entries of the current list chunk
   // Source offsets of a phase's half tiles: K entry ki and V^T entry vi of
@@ -173,33 +179,60 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   struct Src {
     uint32_t kbase, vso, vadd;
   };
-  auto src_of = [&](int hh, int ki, int vi) -> Src {
+  // list entry i (block index; 0 outside [0, n)), uniform over the wavefront
+  auto entry = [&](int i) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane((uint32_t)lcol[(uint32_t)i < (uint32_t)n ? i : 0]);
+  };
+  auto src_from = [&](int hh, int ki, int vi, uint32_t kb, uint32_t vb) -> Src {
     const bool kin = (uint32_t)ki < (uint32_t)n, vin = (uint32_t)vi < (uint32_t)n;
-    const uint32_t kb = (uint32_t)lcol[kin ? ki : 0], vb = (uint32_t)lcol[vin ? vi : 0];
-    const uint32_t kblk = __builtin_amdgcn_readfirstlane(kb < (uint32_t)p.nQB ? kb : 0u);
-    const uint32_t vblk = __builtin_amdgcn_readfirstlane(vb < (uint32_t)p.nQB ? vb : 0u);
+    const uint32_t kblk = kb < (uint32_t)p.nQB ? kb : 0u;
+    const uint32_t vblk = vb < (uint32_t)p.nQB ? vb : 0u;
     Src sr;
     sr.kbase = kin ? (kblk * C::BLK + C::HK * hh) * ks2b : kOOR;
     sr.vso = vin ? (vblk * C::BLK + C::HK * hh) * 2 : 0u;
     sr.vadd = vin ? 0u : kOOR;
     return sr;
   };
-  auto copy_slot = [&](int t, uint8_t *kdst, uint8_t *vdst, const Src &sr) {
-    const int c = wave + C::NW * t;
-    if (t < C::NSK) lds_copy16(krs, lds_addr(kdst) + c * 1024, lo[t] + sr.kbase, 0u);
-    else lds_copy16(vrs, lds_addr(vdst) + (c - C::NKC) * 1024, lo[t] + sr.vadd, sr.vso);
+  auto src_of = [&](int hh, int ki, int vi) -> Src { return src_from(hh, ki, vi, entry(ki), entry(vi)); };
+  // What a softmax step reads from the staged list: its copy sources (K entry
+  // j+2, V^T entry j+1) and its own block and log-weight.  Read one phase
+  // ahead, during the same wavefront's matrix step, so that the softmax step
+  // does not start with an LDS wait behind the matrix steps' operand reads.
+  struct Pre {
+    uint32_t kb, vb, eb;
+    float bias;
+  };
+  auto pre_of = [&](int j) -> Pre {
+    Pre pr;
+    pr.kb = entry(j + 2);
+    pr.vb = entry(j + 1);
+    pr.eb = entry(j);
+    pr.bias = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, lbias[j < n ? j : 0])));
+    return pr;
+  };
+  // copy slot T of a phase into K buffer BK or V^T buffer BV
+  auto copy_slot = [&](auto tc, auto bkc, auto bvc, const Src &sr) {
+    constexpr int T = decltype(tc)::value, BK = decltype(bkc)::value, BV = decltype(bvc)::value;
+    if constexpr (T < C::NSK)
+      lds_copy16_at<(uint32_t)(BK * C::KB + T * C::NQG * 1024)>(krs, wbase, lo[T] + sr.kbase, 0u);
+    else
+      lds_copy16_at<(uint32_t)(BV * C::KB + (T - C::NSK) * C::NQG * 1024)>(vrs, wbase, lo[T] + sr.vadd, sr.vso);
+  };
+  auto copy_all = [&](auto bkc, auto bvc, const Src &sr) {
+    static_for<0, C::NSLOT>([&](auto tc) { copy_slot(tc, bkc, bvc, sr); });
   };
 
-  // End of a phase: this wavefront's LDS reads are done and its copies from
-  // two phases ago have landed; then the barrier.  The empty asm statements
-  // keep the compiler from moving memory accesses across the barrier.
+  // End of a phase: this wavefront's LDS reads are done and every copy it
+  // issued before its latest softmax step (two phases ago at the latest) has
+  // landed; then the barrier.  The empty asm statements keep the compiler
+  // from moving memory accesses across the barrier.
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   auto end_phase = [&]() {
-    __builtin_amdgcn_s_waitcnt(vm_lgkm0_wait_imm(2 * C::NSLOT));
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0_wait_imm(C::NSLOT));
     barrier();
   };
 
@@ -208,16 +241,17 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
   // buffer a step touches is a known object.
   auto half = [&](auto khc) {
     constexpr int KH = decltype(khc)::value;
-    float m_run = 0.f, l_run = 0.f;
+    // Online-softmax state of this lane's query over its key half.  The
+    // running max m_run stays fixed for a whole pass (0 in the first), so O
+    // is only ever written by the MFMAs.  A tile whose probabilities sum past
+    // 2^64, or below 2^-60, is "cold": its max is folded into m_cold (and an
+    // overflow is remembered).  A row that overflowed, or whose total stays
+    // below 2^-60, is computed again from m_cold (second pass).
+    float m_run = 0.f, l_run = 0.f, m_cold = -INFINITY;
+    bool ovf = false;
     f32x16 o[C::DT];
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     f32x16 s[C::MTW];
     bf16x8 pb[C::MTW][2];
-#pragma unroll
-    for (int jj = 0; jj < C::MTW; ++jj) pb[jj][0] = pb[jj][1] = bf16x8{};
 
     // LDS read addresses: K operand (jj, ks) at ka[jj] ^ 32 ks, V^T operand
     // (jj, s2, dt) at (va ^ (64 jj + 32 s2)) + 4096 dt
@@ -243,39 +277,29 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
         asm volatile("" ::"v"(s[jj]));
         asm volatile("" ::"v"(pb[jj][0]), "v"(pb[jj][1]));
       }
-      asm volatile("" ::"v"(m_run), "v"(l_run));
+      asm volatile("" ::"v"(l_run));
     };
 
     // Matrix step: O += V^T P^T (previous tile), then S = K Q^T (this tile);
-    // one 16-byte LDS read per MFMA, the phase's copies spread between them.
-    // Before the first tile pb is zero and the V^T buffer holds zeros; after
-    // the last one S is not used.
-    auto mstep = [&](const uint8_t *vt, const uint8_t *kt, uint8_t *kd, uint8_t *vd, const Src &sr) {
-      constexpr int every = C::NM / C::NSLOT;
-#pragma unroll
-      for (int jj = 0; jj < C::MTW; ++jj)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(vt + ((va ^ (64 * jj + 32 * s2)) + 4096 * dt));
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj][s2], o[dt], 0, 0, 0);
-            const int m = (jj * 2 + s2) * C::DT + dt + 1;
-            if (m % every == 0) copy_slot(m / every - 1, kd, vd, sr);
-          }
+    // one 16-byte LDS read per MFMA.  Before the first tile pb is zero and
+    // the V^T buffer holds zeros; after the last one S is not used.
+    auto mstep = [&](const uint8_t *vt, const uint8_t *kt) {
+      static_for<0, 2 * C::MTW * C::DT>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int jj = i / (2 * C::DT), s2 = (i / C::DT) % 2, dt = i % C::DT;
+        const uint4 a = *reinterpret_cast<const uint4 *>(vt + ((va ^ (64 * jj + 32 * s2)) + 4096 * dt));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[jj][s2], o[dt], 0, 0, 0);
+      });
 #pragma unroll
       for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[jj][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int jj = 0; jj < C::MTW; ++jj) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(kt + (ka[jj] ^ (32 * ks)));
-          s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[jj], 0, 0, 0);
-          const int m = 2 * C::MTW * C::DT + ks * C::MTW + jj + 1;
-          if (m % every == 0) copy_slot(m / every - 1, kd, vd, sr);
-        }
+      static_for<0, C::KS * C::MTW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int ks = i / C::MTW, jj = i % C::MTW;
+        const uint4 a = *reinterpret_cast<const uint4 *>(kt + (ka[jj] ^ (32 * ks)));
+        s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[jj], 0, 0, 0);
+      });
       // keep kRA operand reads in flight ahead of the MFMAs
       constexpr int kRA = 6;
       __builtin_amdgcn_sched_group_barrier(0x100, kRA, 0);
@@ -287,85 +311,56 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
       __builtin_amdgcn_sched_group_barrier(0x008, kRA, 0);
     };
 
-    // softmax step of list entry i: mask, max, lazy rescale, exponentials -> pb,
-    // with the phase's copies spread over the four groups of eight
-    // exponentials
-    auto estep = [&](int i, uint8_t *kd, uint8_t *vd, const Src &sr) {
-      const uint32_t vb = (uint32_t)lcol[i];
-      const float bias = lbias[i];
+    // softmax step of list entry i: mask, exponentials against the fixed
+    // running max -> pb, with the phase's copies spread over the four groups
+    // of eight exponentials; cold tiles fold their max into m_cold
+    auto estep = [&](const Pre &pr, auto bkc, auto bvc, const Src &sr) {
+      const uint32_t vb = pr.eb;
+      const float bias = pr.bias;
       if (vb >= (uint32_t)mlim) {
         asm volatile("");   // keep this a branch: most tiles need no mask
         // keys past N (last block) and, when causal, keys after the query; a
         // block index outside the rows masks every key.  Element e of M tile
-        // jj holds key offset ob + 32 jj + 16 (e >> 3) + (e & 7) in the block.
+        // jj holds key offset ob + 32 jj + 16 (e >> 3) + (e & 7) in the block;
+        // offsets above lim1 (relative to ob) are masked by a min with -inf,
+        // formed from the sign of lim1 - offset (no per-element lane masks).
         const int vbc = vb < (uint32_t)p.nQB ? (int)vb : p.nQB;
         const int kbase = vbc * C::BLK;
         const int lim_n = N - kbase > C::BLK ? C::BLK : (N - kbase < 0 ? 0 : N - kbase);   // offsets >= lim_n: padding
         const int lc = p.causal ? qi - kbase + 1 : C::BLK;                                  // offsets >= lc: after the query
-        const int lim = (lc < lim_n ? lc : lim_n) - ob;
+        const int lim1 = (lc < lim_n ? lc : lim_n) - ob - 1;
 #pragma unroll
         for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (32 * jj + 16 * (e >> 3) + (e & 7) >= lim) s[jj][e] = -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t d = (uint32_t)(lim1 - (32 * jj + 16 * (e >> 3) + (e & 7)));
+            s[jj][e] = fminf(s[jj][e], __uint_as_float((d & 0x80000000u) | 0x7f800000u));
+          }
       }
-      // exponentials against the running max; it is moved only when a lane's
-      // 32 probabilities sum past 32 * 2^8 (some probability above 2^8) or
-      // the lane's sum so far is below 2^-64, and then the tile is redone
-      float nb = bias - m_run;
+      const float nb = bias - m_run;
       float ls = 0.f;
+      static_for<0, 2 * C::MTW>([&](auto gc) {
+        constexpr int gi = decltype(gc)::value;   // exponential group; its copies follow it
+        constexpr int jj = gi / 2, s2 = gi % 2;
+        float pv[8];
 #pragma unroll
-      for (int jj = 0; jj < C::MTW; ++jj)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float pv[8];
-#pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
-          ls += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-          pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                                                             cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
-          const int gi = 2 * jj + s2;   // exponential group; its copies follow it
-          asm volatile("" ::"v"(pb[jj][s2]));
-#pragma unroll
-          for (int t = gi * C::NSLOT / (2 * C::MTW); t < (gi + 1) * C::NSLOT / (2 * C::MTW); ++t)
-            copy_slot(t, kd, vd, sr);
-        }
-      if (__any(ls > 32.f * 256.f || l_run + ls < 0x1p-64f)) {
+        for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
+        ls += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                                                           cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
+        asm volatile("" ::"v"(pb[jj][s2]));
+        static_for<gi * C::NSLOT / (2 * C::MTW), (gi + 1) * C::NSLOT / (2 * C::MTW)>(
+            [&](auto tc) { copy_slot(tc, bkc, bvc, sr); });
+      });
+      const bool over = !(ls <= 0x1p64f);
+      if (__any(over || ls < 0x1p-60f)) {
         float m = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < C::MTW; ++jj)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) m = fmaxf(m, fmaf(s[jj][e], p.c, nb));
-        m = halves_max(m);
-        const float lsum = halves_sum(ls), lrun = halves_sum(l_run);
-        // Raised when a probability may exceed 2^8.  While the sum so far
-        // (this tile included) is below 2^-64 (nothing, or only denormal
-        // probabilities), moved toward the tile max: all the way when nothing
-        // has been accumulated (O and l are zero and are multiplied by 0), by
-        // at most 64 otherwise, so the rescale factor stays finite.
-        float sh = 0.f;
-        if (m > kTau) sh = m;
-        else if (lrun + lsum < 0x1p-64f && m > -INFINITY) sh = lrun == 0.f ? m : fmaxf(m, -64.f);
-        m_run += sh;
-        nb = bias - m_run;
-        const float alpha = lrun == 0.f ? 0.f : __builtin_amdgcn_exp2f(-sh);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-        ls = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < C::MTW; ++jj)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            float pv[8];
-#pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(s[jj][8 * s2 + e8], p.c, nb));
-            ls += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-            pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                                                               cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
-          }
+          for (int e = 0; e < 16; ++e) m = fmaxf(m, fmaf(s[jj][e], p.c, bias));
+        m_cold = fmaxf(m_cold, halves_max(m));
+        ovf = ovf || over;
       }
       l_run += ls;
     };
@@ -373,37 +368,29 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     // Phase loop.  Half 0 runs M(0) E(0) M(1) ... E(n-1) M(n) in phases
     // 0 .. 2n and idles in phase 2n+1; half 1 idles in phase 0 and runs the
     // same steps in phases 1 .. 2n+1.  M(j) reads V^T entry j-1 of this half
-    // from vmine[(j-1) & 1] and K entry j from kmine[j & 1].  Copies of phase
-    // f: half (f odd ? 0 : 1), K entry (f+3)/2 into that half's K buffer
-    // (entry & 1), V^T entry (f+1)/2 into its V^T buffer (entry & 1).  In
-    // phase 2n+1 only half 1 copies (entries past the list, never read).
-    uint8_t *const km0 = KH ? ky0 : kx0, *const km1 = KH ? ky1 : kx1;
-    uint8_t *const vm0 = KH ? vy0 : vx0, *const vm1 = KH ? vy1 : vx1;
-    auto m_phase = [&](int j, auto par) {
+    // from vmine[(j-1) & 1] and K entry j from kmine[j & 1].  The copies of
+    // phase f are those of half (f odd ? 0 : 1), K entry (f+3)/2 into that
+    // half's K buffer (entry & 1), V^T entry (f+1)/2 into its V^T buffer
+    // (entry & 1), and that half runs the phase's softmax step (in phase 0,
+    // where half 1 idles, it only copies): only softmax steps copy, so the
+    // matrix steps issue nothing but LDS reads and MFMAs.  In phase 2n+1
+    // nothing is copied (entries past the list, never read).
+    constexpr int KM0 = KH ? KY0 : KX0, KM1 = KH ? KY1 : KX1;
+    constexpr int VM0 = KH ? VY0 : VX0, VM1 = KH ? VY1 : VX1;
+    auto m_phase = [&](int j, auto par) -> Pre {
       constexpr int P = decltype(par)::value;   // j & 1
-      // phase 2j + KH: half 0 copies into half 1's buffers and vice versa
-      uint8_t *kd, *vd;
-      int hh, ki, vi;
-      if (KH == 0) {   // phase 2j: half 1, K entry j+1, V^T entry j
-        kd = P ? ky0 : ky1;
-        vd = P ? vy1 : vy0;
-        hh = 1, ki = j + 1, vi = j;
-      } else {         // phase 2j+1: half 0, K entry j+2, V^T entry j+1
-        kd = P ? kx1 : kx0;
-        vd = P ? vx0 : vx1;
-        hh = 0, ki = j + 2, vi = j + 1;
-      }
-      const Src sr = src_of(hh, ki, vi);
-      mstep(P ? vm0 : vm1, P ? km1 : km0, kd, vd, sr);
+      const Pre pr = pre_of(j);
+      mstep(smem + (P ? VM0 : VM1) * C::KB, smem + (P ? KM1 : KM0) * C::KB);
       pin_results();
       end_phase();
+      return pr;
     };
-    auto e_phase = [&](int j, auto par) {
+    auto e_phase = [&](int j, auto par, const Pre &pr) {
       constexpr int P = decltype(par)::value;
       // phase 2j+1+KH: this half, K entry j+2 into kmine[j & 1], V^T entry
       // j+1 into vmine[(j+1) & 1]
-      const Src sr = src_of(KH, j + 2, j + 1);
-      estep(j, P ? km1 : km0, P ? vm0 : vm1, sr);
+      const Src sr = src_from(KH, j + 2, j + 1, pr.kb, pr.vb);
+      estep(pr, std::integral_constant<int, P ? KM1 : KM0>(), std::integral_constant<int, P ? VM0 : VM1>(), sr);
       pin_results();
       end_phase();
     };
@@ -412,56 +399,82 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
       using O = std::integral_constant<int, 1>;
       if (KH == 1) {   // phase 0: half 1, K entry 1 into ky1, V^T entry 0 into vy0
         const Src sr = src_of(1, 1, 0);
-#pragma unroll
-        for (int t = 0; t < C::NSLOT; ++t) copy_slot(t, ky1, vy0, sr);
+        copy_all(std::integral_constant<int, KY1>(), std::integral_constant<int, VY0>(), sr);
         end_phase();
       }
       for (int j = 0;; j += 2) {
-        m_phase(j, Z());
+        const Pre p0 = m_phase(j, Z());
         if (j == n) break;
-        e_phase(j, Z());
-        m_phase(j + 1, O());
+        e_phase(j, Z(), p0);
+        const Pre p1 = m_phase(j + 1, O());
         if (j + 1 == n) break;
-        e_phase(j + 1, O());
+        e_phase(j + 1, O(), p1);
       }
       if (KH == 0) barrier();   // phase 2n+1
     };
 
-    for (int c0 = e0; c0 < e1; c0 += C::LIST) {
-      n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
-      if constexpr (kCrm) {
-        if (c0 > 0) bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
-        for (int i = tid; i < n; i += C::NT) lbias[i] = 0.f;
-      } else {
-        for (int i = tid; i < n; i += C::NT) {
-          lcol[i] = col[c0 + i];
-          lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
-        }
-      }
-      __syncthreads();
-      // what the first phases read: K entries 0 and 1 and V^T entry 0 of half
-      // 0, K entry 0 of half 1, and zeros for "V^T entry -1" of both halves
-      // (all eight wavefronts copy, as in a phase)
-      {
-        const Src s0 = src_of(0, 0, 0), s1 = src_of(0, 1, -1), s2 = src_of(1, 0, -1);
+    for (int pass = 0;; ++pass) {
 #pragma unroll
-        for (int t = 0; t < C::NSLOT; ++t) {
-          copy_slot(t, kx0, vx0, s0);
-          copy_slot(t, kx1, vx1, s1);
-          copy_slot(t, ky0, vy1, s2);
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+      l_run = 0.f;
+      m_cold = -INFINITY;
+      ovf = false;
+      for (int c0 = e0; c0 < e1; c0 += C::LIST) {
+        n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
+        if constexpr (kCrm) {
+          if (c0 > 0 || pass > 0) bsa_crm_walk(crow, p.crm_words, p.crm_tail, c0, n, lcol, wave, C::NW, lane);
+          for (int i = tid; i < n; i += C::NT) lbias[i] = 0.f;
+        } else {
+          for (int i = tid; i < n; i += C::NT) {
+            lcol[i] = col[c0 + i];
+            lbias[i] = lw ? lw[c0 + i] * kLog2e : 0.f;
+          }
         }
+        // the first matrix step multiplies pb by the zero "V^T entry -1"
+#pragma unroll
+        for (int jj = 0; jj < C::MTW; ++jj) pb[jj][0] = pb[jj][1] = bf16x8{};
+        __syncthreads();
+        // what the first phases read: K entries 0 and 1 and V^T entry 0 of half
+        // 0, K entry 0 of half 1, and zeros for "V^T entry -1" of both halves
+        // (each wavefront copies its query group's slots of one or two sets)
+        if (KH == 0) {
+          copy_all(std::integral_constant<int, KX0>(), std::integral_constant<int, VX0>(), src_of(0, 0, 0));
+          copy_all(std::integral_constant<int, KY0>(), std::integral_constant<int, VY1>(), src_of(1, 0, -1));
+        } else {
+          copy_all(std::integral_constant<int, KX1>(), std::integral_constant<int, VX1>(), src_of(0, 1, -1));
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        run_half();
+        __builtin_amdgcn_s_waitcnt(0);   // every copy has landed before the buffers are reused
+        __syncthreads();
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      // per query (both lanes of it): l over this key half, cold max, overflow
+      const float lq = halves_sum(l_run);
+      mrg[KH][0][qg][lane] = lq;
+      mrg[KH][1][qg][lane] = m_cold;
+      mrg[KH][2][qg][lane] = halves_max(ovf ? 1.f : 0.f);
+      mrg[KH][3][qg][lane] = m_run;
       __syncthreads();
-      run_half();
-      __builtin_amdgcn_s_waitcnt(0);   // every copy has landed before the buffers are reused
+      if (pass > 0) break;
+      const float mc = fmaxf(mrg[0][1][qg][lane], mrg[1][1][qg][lane]);
+      const bool over = mrg[0][2][qg][lane] + mrg[1][2][qg][lane] > 0.f;
+      const bool need = over || (mrg[0][0][qg][lane] + mrg[1][0][qg][lane] < 0x1p-60f && mc > -INFINITY);
+      const bool wneed = __any(need);
+      if (lane == 0) redo_vote[wave] = wneed ? 1 : 0;
       __syncthreads();
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) any |= redo_vote[w];
+      __syncthreads();   // votes and merge values are read before they are written again
+      if (!any) break;
+      if (need) m_run = mc;   // both halves of the query start from the same max
     }
 
     // merge the two key halves of every query group, normalise, store
-    const float l_w = halves_sum(l_run);
-    uint8_t *const mbuf = qg == 0 ? kx0 : qg == 1 ? kx1 : qg == 2 ? ky0 : ky1;
-    float *scratch = reinterpret_cast<float *>(mbuf);
+    float *scratch = reinterpret_cast<float *>(smem + qg * C::KB);
     if (KH == 1) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -469,17 +482,15 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
         for (int i4 = 0; i4 < 4; ++i4)
           *reinterpret_cast<f32x4 *>(scratch + ((dt * 4 + i4) * 64 + lane) * 4) =
               f32x4{o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
-      mrg_ml[qg][0][lane] = m_run;
-      mrg_ml[qg][1][lane] = l_w;
     }
     __syncthreads();
     if (KH != 0) return;
-    const float m2 = mrg_ml[qg][0][lane];
-    const float l2 = mrg_ml[qg][1][lane];
+    const float l_w = mrg[0][0][qg][lane];
+    const float m2 = mrg[1][3][qg][lane];
+    const float l2 = mrg[1][0][qg][lane];
     // A half with nothing accumulated (l = 0) takes no part, whatever running
-    // max it holds: its max may sit far above the other half's (a fully
-    // masked half keeps its starting max of 0 while the other half's scores
-    // are far below it), and a weight 2^(m_other - m) would then underflow.
+    // max it holds: its max may sit far above the other half's, and a weight
+    // 2^(m_other - m) would then underflow.
     const float m = l_w > 0.f ? (l2 > 0.f ? fmaxf(m_run, m2) : m_run) : m2;
     const float a1 = l_w > 0.f ? __builtin_amdgcn_exp2f(m_run - m) : 0.f;
     const float a2 = l2 > 0.f ? __builtin_amdgcn_exp2f(m2 - m) : 0.f;
