@@ -23,6 +23,11 @@ P = ctypes.c_void_p
 I64 = ctypes.c_int64
 
 
+# A build of oracle.c to load instead of liboracle.so (the sanitizer test
+# runs the pins against an -fsanitize=address,undefined build this way).
+_ALT = os.environ.get("BSA_ORACLE_LIB")
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (OpenMP, -O2)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
@@ -33,12 +38,23 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (every finding fatal) into ``path``.  A process that loads it needs the
+    ASan runtime preloaded (the Python interpreter is not instrumented)."""
+    subprocess.check_call(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=all", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+                           "-o", path, _SRC, "-lm"])
+    return path
+
+
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        path = _ALT or _LIB
+        if not _ALT and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         L.oracle_build_csr.restype = I64
         L.oracle_build_csr.argtypes = [P, P, ctypes.c_float, P, I64, I64, I64, ctypes.c_int,
                                        P, P, P, I64]

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for block-sparse attention workloads.
 
-This module is shared by the GPU path's tests/benchmark and by the CPU
-reference checker.  It only draws random numbers and lays out the *inputs* of
+This module is test and benchmark infrastructure, not part of the shipped
+package: the GPU path's tests and benchmark and the CPU reference checker's
+tests draw their inputs from it.  It only draws random numbers and lays out the *inputs* of
 the path (bf16 Q/K/V bit patterns, block masks, threshold maps, per-block
 log-weight maps, cluster labels).  It contains none of the path's own
 arithmetic: no CSR construction, no permutation, no schedule, no attention.

@@ -6,7 +6,8 @@ import numpy as np
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import pipeline, synth
+from block_sparse_attention_mask_amd import pipeline
+import synth
 
 # bf16 inputs, fp32 accumulation, P and O rounded to bf16.
 MAX_ABS = 2e-2

@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import api, synth
+from block_sparse_attention_mask_amd import api
+import synth
 from parity_common import assert_within, compare_rows, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu

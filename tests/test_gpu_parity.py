@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import api, pipeline, synth
+from block_sparse_attention_mask_amd import api, pipeline
+import synth
 from parity_common import (assert_within, bf16_tensor_to_f32, compare_rows, oracle_csr, oracle_perms, sample_rows,
                            run_gpu)
 
@@ -290,3 +291,30 @@ def test_stage1_schedule_leaves_outputs_unchanged():
     assert not np.array_equal(r1.order.cpu().numpy(), r2.order.cpu().numpy())
     assert np.array_equal(r1.out.cpu().numpy(), r2.out.cpu().numpy())
     assert np.array_equal(r1.lse.cpu().numpy(), r2.lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("block,d,vdm", [(128, 128, True), (128, 64, True), (64, 128, True), (128, 128, False),
+                                         (64, 64, False)])
+def test_minus_inf_log_weights(block, d, vdm):
+    """Log-weights of -inf remove a listed block from the softmax (its
+    exponentials are 0).  Blocks with lw = -inf are scattered over the rows,
+    and one row has -inf on every listed block, the diagonal included: its
+    queries have no allowed key, so O = 0 and LSE = -inf there."""
+    N = 3 * block + 37
+    w = synth.random_case(4242 + block + d + vdm, B=1, Hq=2, Hkv=1, N=N, d=d, block=block, density=0.6,
+                          log_weights=True)
+    rng = np.random.default_rng(7)
+    drop = rng.random(w.lw_map.shape) < 0.3
+    w.lw_map[drop] = -np.inf
+    full = w.nQB + 1                      # head 1, query block 1
+    w.lw_map[full, :] = -np.inf
+    _log("case -inf log-weights block=%d d=%d v_dim_major=%d" % (block, d, vdm))
+    _, res = run_gpu(w, schedule=True, n_xcd=8, v_dim_major=vdm)
+    rows = np.arange(w.B * w.Hq * N, dtype=np.int64)
+    stats = compare_rows(w, res, rows)
+    _log("  %s" % stats)
+    assert_within(stats)
+    out = bf16_tensor_to_f32(res.out).reshape(w.Hq, N, d)
+    lse = res.lse.cpu().numpy().reshape(w.Hq, N)
+    assert np.all(out[1, block:2 * block] == 0)
+    assert np.all(np.isneginf(lse[1, block:2 * block]))

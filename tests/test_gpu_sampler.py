@@ -21,7 +21,8 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import api, pipeline, synth
+from block_sparse_attention_mask_amd import api, pipeline
+import synth
 from parity_common import assert_within, compare_rows, sample_rows
 
 pytestmark = pytest.mark.gpu

@@ -22,7 +22,8 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import api, synth
+from block_sparse_attention_mask_amd import api
+import synth
 
 pytestmark = pytest.mark.gpu
 

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import oracle
-from block_sparse_attention_mask_amd import metrics, synth
+from block_sparse_attention_mask_amd import metrics
+import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "intra_flops.json")
 

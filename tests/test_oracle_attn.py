@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 
 torch.set_default_dtype(torch.float64)
 

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 from test_oracle_csr_sched import keep_matrix
 
 

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 
 
 def qk(seed, B, Hq, Hkv, N, d, scale=1.0):

@@ -19,7 +19,7 @@ import pytest
 from scipy.optimize import brentq
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 
 
 def problem(seed, B=1, Hq=2, Hkv=2, N=1000, block=64, d=16, G=5, spread=1.0):

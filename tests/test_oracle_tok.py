@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from block_sparse_attention_mask_amd import synth
+import synth
 
 
 def rand_qkv(seed, B, Hq, Hkv, N, d):
