@@ -89,6 +89,8 @@ def lib():
         L.oracle_group_mass.restype = ctypes.c_int
         L.oracle_topk.argtypes = [P, I64, I64, I64, P]
         L.oracle_topk.restype = ctypes.c_int
+        L.oracle_stage1_decide.argtypes = [P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P]
+        L.oracle_stage1_decide.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -239,6 +241,33 @@ def spectral_order(row_ptr: np.ndarray, col: np.ndarray, BH: int, nQB: int, nKB:
     if rc:
         raise ValueError("oracle_spectral_order failed: %d" % rc)
     return perm.reshape(BH, nQB), angle.reshape(BH, nQB)
+
+
+# Defaults of the stage-1 skip estimate (WaveAlign adaptive skip):
+# gamma 0.04, the largest relative kernel-time reduction stage 1 gave on
+# MI355X per unit of fresh-block fraction; 2.1e-3 ms per 128x128 block pair
+# on one compute unit (d = 128); stage-1 cost 8.6e-4 ms per query-block row
+# and 3.5e-6 ms per listed block of the largest head per 10 iterations;
+# density threshold 0.10; L2 of one XCD, 4 MiB.
+STAGE1_DEFAULTS = (0.04, 2.1e-3, 8.6e-4, 3.5e-6, 0.10, 4.0 * 1024 * 1024)
+
+
+def stage1_decide(row_ptr, col, BH: int, nQB: int, nKB: int, N: int, d: int, block: int, iters: int,
+                  n_cus: int, params=STAGE1_DEFAULTS):
+    """WaveAlign's adaptive skip of stage 1.  Returns (run: bool, stats dict)."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    assert row_ptr.size == BH * nQB + 1
+    prm = np.ascontiguousarray(params, dtype=np.float64)
+    assert prm.size == 6
+    run = np.zeros(1, dtype=np.int32)
+    st = np.zeros(7, dtype=np.float64)
+    rc = lib().oracle_stage1_decide(_p(row_ptr), _p(col), BH, nQB, nKB, N, d, block, iters, n_cus, _p(prm),
+                                    _p(run), _p(st))
+    if rc:
+        raise ValueError("oracle_stage1_decide failed: %d" % rc)
+    names = ("fresh_fraction", "density", "t_attn_ms", "gain_ms", "cost_ms", "kv_bytes_per_head", "run")
+    return bool(run[0]), dict(zip(names, st.tolist()))
 
 
 def attn_rows(q, k, v, row_ptr, col, lw, block: int, rows: np.ndarray, perm_q=None, perm_k=None,

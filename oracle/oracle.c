@@ -418,6 +418,82 @@ int oracle_spectral_order(const int32_t *row_ptr, const int32_t *col, int64_t BH
 }
 
 /* ------------------------------------------------------------------------ */
+/* WaveAlign adaptive skip of stage 1                                        */
+/* ------------------------------------------------------------------------ */
+/* WaveAlign, section IV-E (Runtime Coordination) and section VI-F with
+ * Figure 13: the reordering is bypassed when its estimated latency reduction
+ * does not exceed its overhead; reordering was skipped at low retained
+ * densities (1.7 %, 6.7 %) and enabled from 14.5 %.  The pages give the
+ * estimate in words only; this is the reading, step by step:
+ *   nnz   = listed blocks (entries in [0, nKB)) over all BH heads;
+ *   nmax  = the largest per-head nnz (heads are reordered in parallel);
+ *   fresh = sum over rows of the blocks the row lists and the row before it
+ *           in the same head does not (the first row of a head: all), so
+ *           f = fresh / nnz is the share of K/V block visits that the
+ *           current order does not pair with the previous row;
+ *   density = nnz / (BH nQB nKB);
+ *   t_attn  = nnz * tile_ms * (block/128)^2 * (d/128) / n_cus, the attention
+ *             time at the measured cost of one block pair on one compute unit;
+ *   gain    = gamma * f * t_attn;
+ *   cost    = (iters / 10) * (row_ms * nQB + nnz_ms * nmax);
+ *   footprint = 2 * N * d * 2 bytes of K and V per KV head.
+ * Stage 1 runs when footprint > l2_bytes (otherwise every block stays in the
+ * L2 whatever the order), density >= density_min, gain > cost, and the
+ * stage-1 kernel supports the shape (nQB, nKB <= 1024, nKB * ceil(nQB/32)
+ * and nQB * ceil(nKB/32) <= 12288).  prm = {gamma, tile_ms, row_ms, nnz_ms,
+ * density_min, l2_bytes}.  stats (out, 7 doubles): f, density, t_attn,
+ * gain, cost, footprint, and the decision as 0/1. */
+int oracle_stage1_decide(const int32_t *row_ptr, const int32_t *col, int64_t BH, int64_t nQB, int64_t nKB,
+                         int64_t N, int64_t d, int64_t block, int64_t iters, int64_t n_cus, const double *prm,
+                         int32_t *run, double *stats) {
+  if (!row_ptr || !col || !prm || !run || BH <= 0 || nQB <= 0 || nKB <= 0 || N <= 0 || d <= 0 ||
+      block <= 0 || iters < 1 || n_cus <= 0)
+    return OR_ERR_ARG;
+  int64_t nnz = 0, nmax = 0, fresh = 0;
+  for (int64_t h = 0; h < BH; ++h) {
+    int64_t nh = 0;
+    for (int64_t u = 0; u < nQB; ++u) {
+      const int64_t r = h * nQB + u;
+      for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+        const int32_t v = col[e];
+        if (v < 0 || v >= nKB) continue;
+        ++nh;
+        int in_prev = 0;
+        if (u > 0)
+          for (int64_t e2 = row_ptr[r - 1]; e2 < row_ptr[r]; ++e2)
+            if (col[e2] == v) in_prev = 1;
+        if (!in_prev) ++fresh;
+      }
+    }
+    nnz += nh;
+    if (nh > nmax) nmax = nh;
+  }
+  const double gamma = prm[0], tile_ms = prm[1], row_ms = prm[2], nnz_ms = prm[3], density_min = prm[4],
+               l2_bytes = prm[5];
+  const double f = nnz > 0 ? (double)fresh / (double)nnz : 0.0;
+  const double density = (double)nnz / ((double)BH * (double)nQB * (double)nKB);
+  const double bs = (double)block / 128.0;
+  const double t_attn = (double)nnz * tile_ms * bs * bs * ((double)d / 128.0) / (double)n_cus;
+  const double gain = gamma * f * t_attn;
+  const double cost = ((double)iters / 10.0) * (row_ms * (double)nQB + nnz_ms * (double)nmax);
+  const double footprint = 4.0 * (double)N * (double)d;
+  const int64_t w1 = (nQB + 31) / 32, w2 = (nKB + 31) / 32;
+  const int supported = nQB <= 1024 && nKB <= 1024 && nKB * w1 <= 12288 && nQB * w2 <= 12288;
+  const int go = supported && footprint > l2_bytes && density >= density_min && gain > cost;
+  *run = go;
+  if (stats) {
+    stats[0] = f;
+    stats[1] = density;
+    stats[2] = t_attn;
+    stats[3] = gain;
+    stats[4] = cost;
+    stats[5] = footprint;
+    stats[6] = (double)go;
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* attention                                                                 */
 /* ------------------------------------------------------------------------ */
 /* rows[i] = (b * Hq + h) * N + t with t an original (unpermuted) token index.
