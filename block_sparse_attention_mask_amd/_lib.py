@@ -23,7 +23,8 @@ BSA_V_DIM_MAJOR = 1
 EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_crm_build", "bsa_crm_row_ptr",
            "bsa_crm_to_csr", "bsa_segment_offsets", "bsa_segment_means", "bsa_is_sample", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
-           "bsa_attn_fwd", "bsa_attn_tok_fwd", "bsa_group_mass", "bsa_topk_rows",
+           "bsa_attn_fwd", "bsa_attn_tok_fwd", "bsa_group_mass", "bsa_topk_rows", "bsa_stage1_decide",
+           "bsa_stage1_default_params",
            "bsa_device_cus", "bsa_device_clock_khz", "bsa_clock_probe")
 
 
@@ -42,6 +43,11 @@ class AttnArgs(ctypes.Structure):
         ("crm", P),
         ("gather_perm_q", P),
     ]
+
+
+class Stage1Params(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_double), ("tile_ms", ctypes.c_double), ("row_ms", ctypes.c_double),
+                ("nnz_ms", ctypes.c_double), ("density_min", ctypes.c_double), ("l2_bytes", ctypes.c_double)]
 
 
 class TokArgs(ctypes.Structure):
@@ -122,7 +128,12 @@ def load():
         L.bsa_schedule.restype = ctypes.c_int
         L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, P]
         L.bsa_spectral_order.restype = ctypes.c_int
-        L.bsa_spectral_order.argtypes = [P, P, I32, I32, I32, I32, P, P, P]
+        L.bsa_spectral_order.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
+        L.bsa_stage1_default_params.restype = None
+        L.bsa_stage1_default_params.argtypes = [ctypes.POINTER(Stage1Params)]
+        L.bsa_stage1_decide.restype = ctypes.c_int
+        L.bsa_stage1_decide.argtypes = [P, P, I32, I32, I32, I64, I32, I32, I32, I32,
+                                        ctypes.POINTER(Stage1Params), P, P, P]
         L.bsa_attn_fwd.restype = ctypes.c_int
         L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
         L.bsa_clock_probe.restype = ctypes.c_int

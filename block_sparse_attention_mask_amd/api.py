@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import AttnArgs, I64, I64x3, MassArgs, TokArgs, check, load
+from ._lib import AttnArgs, I64, I64x3, MassArgs, Stage1Params, TokArgs, check, load
 
 __all__ = ["version", "csr_count", "csr_fill", "build_csr", "perm_from_labels", "permute_rows",
            "unpermute_rows", "transpose_rows", "schedule", "attn_fwd", "device_cus", "crm_build",
@@ -315,18 +315,63 @@ def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_ro
 
 
 def spectral_order(row_ptr: torch.Tensor, col: torch.Tensor, BH: int, nQB: int, nKB: int, iters: int = 10,
-                   want_angle: bool = False, stream=None):
+                   want_angle: bool = False, enable: Optional[torch.Tensor] = None, stream=None):
     """WaveAlign stage-1 order of every head's query blocks: (perm int32
-    [BH][nQB], angle float64 [BH][nQB] or None)."""
+    [BH][nQB], angle float64 [BH][nQB] or None).  With ``enable`` (device
+    int32 [1], e.g. stage1_decide's decision) holding 0 the order is the
+    identity and nothing is computed."""
     _dev(row_ptr, "row_ptr", torch.int32)
     _dev(col, "col", torch.int32)
+    if enable is not None:
+        _dev(enable, "enable", torch.int32)
     if row_ptr.numel() != BH * nQB + 1:
         raise ValueError("row_ptr must hold BH*nQB + 1 entries")
     perm = torch.empty((BH, nQB), dtype=torch.int32, device=row_ptr.device)
     angle = torch.empty((BH, nQB), dtype=torch.float64, device=row_ptr.device) if want_angle else None
     check("bsa_spectral_order", load().bsa_spectral_order(_ptr(row_ptr), _ptr(col), BH, nQB, nKB, int(iters),
-                                                          _ptr(perm), _ptr(angle), _stream(stream)))
+                                                          _ptr(perm), _ptr(angle), _ptr(enable),
+                                                          _stream(stream)))
     return perm, angle
+
+
+def spectral_supported(nQB: int, nKB: int) -> bool:
+    """The shapes bsa_spectral_order accepts (its LDS bitmask limits)."""
+    return (nQB <= 1024 and nKB <= 1024 and nKB * ((nQB + 31) // 32) <= 12288
+            and nQB * ((nKB + 31) // 32) <= 12288)
+
+
+STAGE1_PARAM_NAMES = ("gamma", "tile_ms", "row_ms", "nnz_ms", "density_min", "l2_bytes")
+STAGE1_STAT_NAMES = ("fresh_fraction", "density", "t_attn_ms", "gain_ms", "cost_ms", "kv_bytes_per_head", "run")
+
+
+def stage1_default_params() -> dict:
+    p = Stage1Params()
+    load().bsa_stage1_default_params(ctypes.byref(p))
+    return {n: getattr(p, n) for n in STAGE1_PARAM_NAMES}
+
+
+def stage1_decide(row_ptr: torch.Tensor, col: torch.Tensor, BH: int, nQB: int, nKB: int, N: int, d: int,
+                  block: int, iters: int = 10, n_cus: int = 0, params: Optional[dict] = None, stream=None):
+    """WaveAlign's adaptive skip: (decision int32 [1], stats float64 [7]),
+    both on the device (no synchronisation).  n_cus = 0: the device's
+    compute units.  params: overrides of stage1_default_params()."""
+    _dev(row_ptr, "row_ptr", torch.int32)
+    _dev(col, "col", torch.int32)
+    if row_ptr.numel() != BH * nQB + 1:
+        raise ValueError("row_ptr must hold BH*nQB + 1 entries")
+    prm = None
+    if params is not None:
+        vals = stage1_default_params()
+        vals.update(params)
+        prm = Stage1Params(*[float(vals[n]) for n in STAGE1_PARAM_NAMES])
+    dec = torch.empty(1, dtype=torch.int32, device=row_ptr.device)
+    stats = torch.empty(7, dtype=torch.float64, device=row_ptr.device)
+    cus = int(n_cus) if n_cus else device_cus()
+    check("bsa_stage1_decide", load().bsa_stage1_decide(_ptr(row_ptr), _ptr(col), BH, nQB, nKB, int(N), int(d),
+                                                        int(block), int(iters), cus,
+                                                        ctypes.byref(prm) if prm is not None else None,
+                                                        _ptr(dec), _ptr(stats), _stream(stream)))
+    return dec, stats
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optional[torch.Tensor],

@@ -53,13 +53,21 @@ __device__ Sums block_sum2(double a, double b, double *red) {
 __global__ __launch_bounds__(kThreads) void spectral_order_kernel(const int32_t *__restrict__ row_ptr,
                                                                   const int32_t *__restrict__ col, int nQB,
                                                                   int nKB, int iters, int32_t *__restrict__ perm,
-                                                                  double *__restrict__ angle) {
+                                                                  double *__restrict__ angle,
+                                                                  const int32_t *__restrict__ enable) {
   __shared__ uint32_t bits[kMaxWords];     // bits[v * nw + u / 32] bit u % 32: block v listed in row u
   __shared__ uint32_t rbits[kMaxWords];    // rbits[u * nwk + v / 32] bit v % 32: the same, row-major
   __shared__ double x1[kMaxRows], x2[kMaxRows], z1[kMaxRows], z2[kMaxRows], mu[kMaxRows];
   __shared__ double red[2 * kThreads];
   const int t = threadIdx.x;
   const int64_t bh = blockIdx.x;
+  if (enable && enable[0] == 0) {   // the adaptive skip decided against stage 1: identity order
+    for (int u = t; u < nQB; u += kThreads) {
+      perm[bh * nQB + u] = u;
+      if (angle) angle[bh * nQB + u] = 0.0;
+    }
+    return;
+  }
   const int32_t *rp = row_ptr + bh * nQB;
   const int nw = (nQB + 31) / 32, nwk = (nKB + 31) / 32;
 
@@ -173,14 +181,14 @@ __global__ __launch_bounds__(kThreads) void spectral_order_kernel(const int32_t 
 
 extern "C" int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, int32_t nQB,
                                   int32_t nKB, int32_t iters, int32_t *perm, double *angle,
-                                  bsa_stream_t stream) {
+                                  const int32_t *enable, bsa_stream_t stream) {
   if (!row_ptr || !col || !perm || BH <= 0 || nQB <= 0 || nKB <= 0 || iters < 1) return BSA_ERR_ARG;
   if (nQB > kMaxRows || nKB > kMaxRows || (int64_t)nKB * ((nQB + 31) / 32) > kMaxWords ||
       (int64_t)nQB * ((nKB + 31) / 32) > kMaxWords)
     return BSA_ERR_UNSUPPORTED;
   if ((int64_t)BH * nQB >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(spectral_order_kernel, dim3((unsigned)BH), dim3(kThreads), 0, bsa_hip_stream(stream), row_ptr,
-                     col, nQB, nKB, iters, perm, angle);
+                     col, nQB, nKB, iters, perm, angle, enable);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

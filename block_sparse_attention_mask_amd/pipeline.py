@@ -87,16 +87,42 @@ class StepResult:
     perm_q: Optional[torch.Tensor] = None
     perm_k: Optional[torch.Tensor] = None
     crm: Optional[torch.Tensor] = None
+    stage1_decision: Optional[torch.Tensor] = None   # device int32 [1] (adaptive skip)
+    stage1_stats: Optional[torch.Tensor] = None      # device float64 [7]
+
+
+def _stage1_order(dw: DeviceWorkload, row_ptr, col, stage1: str, iters: int, stream):
+    """WaveAlign stage 1 in front of the schedule: "off" (no order), "on"
+    (the polar spectral order), or "auto" (the adaptive skip decides on the
+    device whether the order is computed; when it is not, the order is the
+    identity and the schedule equals the "off" one).  Returns (row_perm,
+    decision, stats)."""
+    if stage1 == "off":
+        return None, None, None
+    if stage1 not in ("on", "auto"):
+        raise ValueError("stage1 must be 'off', 'on' or 'auto'")
+    dec = stats = None
+    if stage1 == "auto" and not api.spectral_supported(dw.nQB, dw.nQB):
+        return None, None, None   # the skip would decide against it: stage 1 cannot run on this shape
+    if stage1 == "auto":
+        dec, stats = api.stage1_decide(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, dw.N, dw.d, dw.block, iters,
+                                       stream=stream)
+    perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, iters, enable=dec, stream=stream)
+    return perm, dec, stats
 
 
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
-            v_dim_major: bool = True, stream=None, stage1_iters: int = 0, crm: bool = False,
-            sampler: Optional[dict] = None, fuse_gather: bool = True, overlap: bool = False) -> StepResult:
+            v_dim_major: bool = True, stream=None, stage1: str = "auto", stage1_iters: int = 10,
+            crm: bool = False, sampler: Optional[dict] = None, fuse_gather: bool = True,
+            overlap: bool = False) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
-    recorded around the attention launch on the same stream.  With
-    ``stage1_iters`` > 0 the schedule starts from the polar spectral order of
-    each head's query blocks (that many subspace iterations).  With ``crm``
+    recorded around the attention launch on the same stream.  ``stage1``
+    selects WaveAlign's stage 1 in front of the schedule: "auto" (the
+    adaptive skip decides on the device), "on" or "off"; ``stage1_iters``
+    subspace iterations when it runs.  With CRM lists "auto" means "off"
+    (the decision reads CSR columns, which CRM rows only give after a host
+    round trip).  With ``crm``
     the lists are CRM rows (no log-weights, dim-major V); their sizes are
     known up front, so this path makes no host synchronisation.  With
     ``overlap`` the permutations, gathers and transposes run on a second
@@ -109,10 +135,10 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     crm_rows = None
     if sampler is not None:
         return _forward_sampled(dw, sampler, schedule, n_xcd, wave_rows, fuse_scatter, want_lse, attn_events,
-                                stream)
-    if overlap and not crm and stage1_iters == 0:
+                                stream, stage1, stage1_iters)
+    if overlap and not crm:
         return _forward_overlapped(dw, schedule, n_xcd, wave_rows, fuse_scatter, fuse_gather, want_lse,
-                                   attn_events, v_dim_major, stream)
+                                   attn_events, v_dim_major, stream, stage1, stage1_iters)
     if crm:
         if dw.lw_map is not None or not v_dim_major:
             raise ValueError("CRM lists carry no log-weights and need dim-major V")
@@ -134,16 +160,15 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             v = api.permute_rows(dw.v, perm_k, stream=stream)
     if v_dim_major:
         v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=stream)
-    order = None
+    order = dec = stats = None
     if schedule:
         row_perm = None
-        if stage1_iters > 0:
-            cols = col
-            if crm:
-                _, nnz = api.crm_row_ptr(crm_rows, dw.nQB, row_ptr=row_ptr, stream=stream)
-                cols = api.crm_to_csr(crm_rows, dw.nQB, row_ptr, nnz, stream=stream)
-            row_perm, _ = api.spectral_order(row_ptr, cols, dw.B * dw.Hq, dw.nQB, dw.nQB, stage1_iters,
-                                             stream=stream)
+        if crm and stage1 == "on":
+            _, nnz = api.crm_row_ptr(crm_rows, dw.nQB, row_ptr=row_ptr, stream=stream)
+            cols = api.crm_to_csr(crm_rows, dw.nQB, row_ptr, nnz, stream=stream)
+            row_perm, _, _ = _stage1_order(dw, row_ptr, cols, "on", stage1_iters, stream)
+        elif not crm:
+            row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
                              row_perm=row_perm)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
@@ -162,11 +187,12 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows, dec, stats)
 
 
 def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: int, wave_rows: int,
-                     fuse_scatter: bool, want_lse: bool, attn_events, stream) -> StepResult:
+                     fuse_scatter: bool, want_lse: bool, attn_events, stream, stage1: str,
+                     stage1_iters: int) -> StepResult:
     """labels -> perms; Q/K gathered, V gathered and transposed; query-group
     and tile centroids; importance-sampled mask and log-weights -> CSR;
     schedule; attention with fused scatter-back."""
@@ -183,9 +209,11 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
     mask, lw_map, _ = api.is_sample(qbar, kbar, q_seg, sampler["uoff"], dw.B, dw.Hq, dw.Hkv, dw.N, dw.block,
                                     sampler["m_exact"], sampler["m_sample"], stream=stream)
     row_ptr, col, lw = api.build_csr(mask, None, 0.0, lw_map, dw.nQB, True, stream=stream)
-    order = None
+    order = dec = stats = None
     if schedule:
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream)
+        row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
+                             row_perm=row_perm)
     sperm = perm_q if fuse_scatter else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
@@ -200,11 +228,12 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats)
 
 
 def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_rows: int, fuse_scatter: bool,
-                        fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream) -> StepResult:
+                        fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream, stage1: str,
+                        stage1_iters: int) -> StepResult:
     """The same step with two streams: [key labels -> perm_k, K gather, V
     gather + transpose] on a side stream beside [query labels -> perm_q,
     mask -> CSR without a host round trip, schedule] on the caller's stream;
@@ -230,9 +259,11 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
             q = api.permute_rows(dw.q, perm_q, stream=main)
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag, sync=False,
                                      stream=main)
-    order = None
+    order = dec = stats = None
     if schedule:
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main)
+        row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, main)
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main,
+                             row_perm=row_perm)
     main.wait_stream(side)
     for t in (perm_k, k, v):
         if t is not None:
@@ -252,4 +283,4 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats)

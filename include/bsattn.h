@@ -197,12 +197,54 @@ int bsa_transpose_rows(const void *src, void *dst, const int32_t *perm, int32_t 
  * outside [0, nKB) are ignored).  perm: device int32 [BH][nQB] (output):
  * perm[h][p] = query block at position p, a permutation of 0..nQB-1 per head.
  * angle: device float64 [BH][nQB] (output, may be NULL): the angle of each
- * query block.  nQB, nKB <= 1024, nKB * ceil(nQB / 32) <= 12288 and
- * nQB * ceil(nKB / 32) <= 12288 (e.g. 614 x 614 or 512 x 768), else
- * BSA_ERR_UNSUPPORTED; iters >= 1.  Asynchronous.
+ * query block.  enable: device int32 [1] or NULL; when it is given and holds
+ * 0 (the adaptive skip's decision, bsa_stage1_decide) the order is not
+ * computed: perm is the identity and angle (when given) is 0, so a schedule
+ * built from it equals the one built without a stage-1 order.  nQB, nKB <=
+ * 1024, nKB * ceil(nQB / 32) <= 12288 and nQB * ceil(nKB / 32) <= 12288
+ * (e.g. 614 x 614 or 512 x 768), else BSA_ERR_UNSUPPORTED; iters >= 1.
+ * Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, int32_t nQB, int32_t nKB,
-                       int32_t iters, int32_t *perm, double *angle, bsa_stream_t stream);
+                       int32_t iters, int32_t *perm, double *angle, const int32_t *enable,
+                       bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * WaveAlign adaptive skip: should stage 1 run for these lists?
+ *
+ * Source: WaveAlign, section IV-E (Runtime Coordination: the skip module
+ * bypasses the reordering when its estimated latency reduction does not
+ * exceed its overhead) and section VI-F with Figure 13 (skipped at low
+ * retained densities, enabled from 14.5 %).  The pages state the rule in
+ * words; this estimate is the library's reading of it, computed on the
+ * device so that no host round trip is needed.
+ *
+ * Over the BH heads' CSR rows (row_ptr device int32 [BH*nQB + 1], col device
+ * int32, every row ascending; entries outside [0, nKB) are not counted):
+ * nnz = listed blocks, nmax = the largest per-head nnz, fresh = entries a
+ * row lists that the previous row of its head does not (all of the first
+ * row's).  With f = fresh/nnz, density = nnz/(BH nQB nKB),
+ * t_attn = nnz tile_ms (block/128)^2 (d/128) / n_cus (ms), gain = gamma f
+ * t_attn, cost = (iters/10)(row_ms nQB + nnz_ms nmax) (ms): stage 1 runs when
+ * 4 N d (bytes of K and V of a head) > l2_bytes, density >= density_min,
+ * gain > cost, and bsa_spectral_order supports (nQB, nKB).
+ * params: host pointer or NULL for the defaults (bsa_stage1_default_params:
+ * gamma 0.04, tile_ms 2.1e-3, row_ms 8.6e-4, nnz_ms 3.5e-6, density_min
+ * 0.10, l2_bytes 4 MiB, measured on MI355X).  decision: device int32 [1]
+ * (output, 0 or 1).  stats: device float64 [7] (output, may be NULL): f,
+ * density, t_attn, gain, cost, K/V bytes per head, decision.
+ * BSA_ERR_ARG for NULL pointers or non-positive sizes / iters / n_cus;
+ * BSA_ERR_UNSUPPORTED for BH*nQB >= 2^31.  Asynchronous (one workgroup
+ * walks all heads; its reductions run in a fixed order).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  double gamma, tile_ms, row_ms, nnz_ms, density_min, l2_bytes;
+} bsa_stage1_params;
+
+void bsa_stage1_default_params(bsa_stage1_params *params);
+int bsa_stage1_decide(const int32_t *row_ptr, const int32_t *col, int32_t BH, int32_t nQB, int32_t nKB, int64_t N,
+                      int32_t d, int32_t block, int32_t iters, int32_t n_cus, const bsa_stage1_params *params,
+                      int32_t *decision, double *stats, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Segment offsets of labelled tokens (centroid groups).

@@ -89,13 +89,13 @@ def test_schedule_argument_errors(L):
 
 
 def test_spectral_order_argument_errors(L):
-    assert L.bsa_spectral_order(None, FAKE, 4, 100, 100, 10, FAKE, None, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 0, FAKE, None, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 10, None, None, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_spectral_order(FAKE, FAKE, 0, 100, 100, 10, FAKE, None, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1025, 100, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
-    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1024, 1024, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
-    assert L.bsa_spectral_order(FAKE, FAKE, 4, 700, 700, 10, FAKE, None, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_spectral_order(None, FAKE, 4, 100, 100, 10, FAKE, None, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 0, FAKE, None, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 100, 100, 10, None, None, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 0, 100, 100, 10, FAKE, None, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1025, 100, 10, FAKE, None, None, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 1024, 1024, 10, FAKE, None, None, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_spectral_order(FAKE, FAKE, 4, 700, 700, 10, FAKE, None, None, None) == _lib.BSA_ERR_UNSUPPORTED
 
 
 def test_clock_probe_argument_errors(L):
@@ -266,3 +266,21 @@ def test_attn_argument_errors(L, kw, code):
     a = _args(**kw)
     assert L.bsa_attn_fwd(ctypes.byref(a), None) == code
     assert L.bsa_attn_fwd(None, None) == _lib.BSA_ERR_ARG
+
+
+def test_stage1_decide_argument_errors(L):
+    ok = (FAKE, FAKE, 4, 100, 100, 12800, 128, 128, 10, 256, None, FAKE, None, None)
+    for i, bad in [(0, None), (1, None), (11, None), (2, 0), (3, 0), (4, 0), (5, 0), (6, 0), (7, 0), (8, 0),
+                   (9, 0)]:
+        a = list(ok)
+        a[i] = bad
+        assert L.bsa_stage1_decide(*a) == _lib.BSA_ERR_ARG, i
+    assert L.bsa_stage1_decide(FAKE, FAKE, 1 << 16, 1 << 15, 100, 12800, 128, 128, 10, 256, None, FAKE, None,
+                               None) == _lib.BSA_ERR_UNSUPPORTED
+
+
+def test_stage1_default_params(L):
+    p = _lib.Stage1Params()
+    L.bsa_stage1_default_params(ctypes.byref(p))
+    import oracle
+    assert (p.gamma, p.tile_ms, p.row_ms, p.nnz_ms, p.density_min, p.l2_bytes) == oracle.STAGE1_DEFAULTS

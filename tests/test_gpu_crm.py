@@ -133,7 +133,7 @@ def test_crm_long_rows_span_list_chunks(block, d, nblocks):
 def test_crm_stage1_schedule_matches_csr():
     w = synth.random_case(950, B=1, Hq=2, Hkv=2, N=1500, d=128, block=128, density=0.3)
     _log("case crm stage-1 schedule")
-    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1_iters=6)
-    _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1_iters=6, crm=True)
+    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1="on", stage1_iters=6)
+    _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1="on", stage1_iters=6, crm=True)
     assert torch.equal(r_crm.order, r_csr.order)
     assert torch.equal(r_crm.out, r_csr.out)
