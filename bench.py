@@ -135,6 +135,7 @@ def main():
     torch.cuda.synchronize()
     rp = res.row_ptr.cpu().numpy()
     col = res.col[:int(rp[-1])].cpu().numpy()   # col is sized by its bound
+    stage1 = stage1_record(res)
     pairs = metrics.count_pairs(rp, col, w.N, w.block, w.causal)
     eff_flops = 4.0 * w.d * pairs
     nnz = int(rp[-1])
@@ -246,6 +247,7 @@ def main():
                         "l2_flushed_ms": attn_solo["flushed_ms"]},
         "device": device_info(torch),
         "stages_ms": stages,
+        "stage1_adaptive_skip": stage1,
         "crm_lists": crm,
         "importance_sampler": sampled,
         "token_sets": token_sets,
@@ -655,6 +657,18 @@ def summarize_profile(d):
     print(json.dumps(rec, indent=1))
 
 
+def stage1_record(res):
+    """The adaptive skip's statistics and decision for WaveAlign stage 1 (the
+    pass's bsa_stage1_decide output), or None when it did not run."""
+    if res.stage1_stats is None:
+        return None
+    from block_sparse_attention_mask_amd import api
+    st = res.stage1_stats.cpu().numpy()
+    rec = {n: round(float(v), 6) for n, v in zip(api.STAGE1_STAT_NAMES, st)}
+    rec["run"] = bool(rec["run"])
+    return rec
+
+
 def workload_name(cfg):
     return {
         "clustered": "Wan2.1-14B 720p video DiT self-attention, clustered+permuted block-sparse "
@@ -669,7 +683,7 @@ def workload_name(cfg):
 def stage_times(pipeline, dw, args, torch):
     from block_sparse_attention_mask_amd import api
     s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     torch.cuda.synchronize()
     ev[0].record(s)
     row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
@@ -681,13 +695,19 @@ def stage_times(pipeline, dw, args, torch):
         k = api.permute_rows(dw.k, pk)
     v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
     ev[2].record(s)
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd)
+    row_perm = None
+    if api.spectral_supported(dw.nQB, dw.nQB):
+        dec, _ = api.stage1_decide(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, dw.N, dw.d, dw.block, 10)
+        row_perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, 10, enable=dec)
     ev[3].record(s)
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm)
+    ev[4].record(s)
     api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
                  gather_perm_q=pq, causal=dw.causal, v_dim_major=True)
-    ev[4].record(s)
+    ev[5].record(s)
     torch.cuda.synchronize()
-    names = ["mask_to_csr", "perm_k_gather_and_v_transpose", "schedule", "attention_fused_gather_scatter"]
+    names = ["mask_to_csr", "perm_k_gather_and_v_transpose", "stage1_adaptive_skip", "schedule",
+             "attention_fused_gather_scatter"]
     return {n: round(ev[i].elapsed_time(ev[i + 1]), 4) for i, n in enumerate(names)}
 
 
@@ -814,7 +834,8 @@ def workload_line(cfg, args, torch, with_oracle=True):
             "nnz_blocks": nnz, "block_density": round(nnz / float(w.R * w.nKB), 5), "allowed_pairs": int(pairs),
             "effective_gflop": round(flop / 1e9, 3), "kernel": attn_kernel_name(w.block, w.d),
             "kernel_alone_median50_ms": solo["median_ms"], "l2_flushed_ms": solo["flushed_ms"],
-            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "stage1_adaptive_skip": stage1_record(res)}
     log("%s: kernel %.3f ms (median of 50) -> %.1f TFLOPS" % (cfg, solo["median_ms"], tf))
     if with_oracle:
         line["cpu_baseline"] = oracle_leg(w, res.out, res.lse, (rp, col), torch)
