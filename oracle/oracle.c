@@ -42,7 +42,10 @@
  *                     NNZ-guided intra-wave alignment), then the launch-index
  *                     remap that gives each XCD a contiguous run.
  *                     An optional per-head row order (below) replaces the
- *                     query-block order inside each segment.
+ *                     query-block order inside each segment.  With a head
+ *                     step of 2 only the first head of each pair of query
+ *                     heads that share a KV head is scheduled (one launch
+ *                     serves the pair's identical rows).
  *  oracle_spectral_order
  *                     WaveAlign stage 1 (section IV-C): rank-2 embedding of
  *                     each head's mask rows by matrix-free centred subspace
@@ -258,10 +261,12 @@ int oracle_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_
  * then dealt so that launch index i runs logical position start(i % n_xcd) +
  * i / n_xcd, where XCD x receives the x-th contiguous slice. */
 int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t nQB,
-                    int64_t W, int64_t n_xcd, const int32_t *row_perm, int32_t *order) {
+                    int64_t W, int64_t n_xcd, const int32_t *row_perm, int64_t head_step, int32_t *order) {
   if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W <= 0)
     return OR_ERR_ARG;
-  int64_t G = Hq / Hkv, R = B * Hq * nQB, seg = G * nQB;
+  if (head_step < 1 || (Hq / Hkv) % head_step) return OR_ERR_ARG;
+  /* rows scheduled: heads g*G + j with j a multiple of head_step */
+  int64_t G = Hq / Hkv, Gs = G / head_step, R = B * Hkv * Gs * nQB, seg = Gs * nQB;
   int32_t *logical = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
   key_idx *buf = (key_idx *)malloc(sizeof(key_idx) * (size_t)W);
   if (!logical || !buf) return OR_ERR_ARG;
@@ -269,8 +274,8 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
   for (int64_t b = 0; b < B; ++b)
     for (int64_t g = 0; g < Hkv; ++g)
       for (int64_t u = 0; u < nQB; ++u)
-        for (int64_t j = 0; j < G; ++j) {
-          int64_t h = b * Hq + g * G + j;
+        for (int64_t j = 0; j < Gs; ++j) {
+          int64_t h = b * Hq + g * G + j * head_step;
           int64_t uu = row_perm ? row_perm[h * nQB + u] : u;
           logical[pos++] = (int32_t)(h * nQB + uu);
         }

@@ -129,14 +129,15 @@ def test_perm_matches_stable_argsort():
     assert np.all(np.sort(perm, 1) == np.arange(1000)[None])
 
 
-def sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm=None):
+def sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, row_perm=None, head_step=1):
     G = Hq // Hkv
     nnz = np.diff(row_ptr)
     logical = []
     blk = (lambda h, u: u) if row_perm is None else (lambda h, u: int(row_perm[h][u]))
     for b in range(B):
         for g in range(Hkv):
-            seg = [(b * Hq + g * G + j) * nQB + blk(b * Hq + g * G + j, u) for u in range(nQB) for j in range(G)]
+            seg = [(b * Hq + g * G + j) * nQB + blk(b * Hq + g * G + j, u) for u in range(nQB)
+                   for j in range(0, G, head_step)]
             for s in range(0, len(seg), W):
                 bucket = seg[s:s + W]
                 logical += [r for _, _, r in sorted((-int(nnz[r]), i, r) for i, r in enumerate(bucket))]
@@ -173,6 +174,21 @@ def test_schedule_with_row_order_matches_brute_force(B, Hq, Hkv, nQB, W, n_xcd):
                                   oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd))
     if W == 1 and n_xcd == 1 and Hq == Hkv:
         np.testing.assert_array_equal(order, (np.arange(B * Hq)[:, None] * nQB + row_perm).reshape(-1))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nQB,W,n_xcd", [(1, 4, 2, 37, 8, 1), (2, 8, 2, 20, 16, 8), (1, 32, 8, 64, 2048, 8)])
+def test_schedule_of_head_pairs_matches_brute_force(B, Hq, Hkv, nQB, W, n_xcd):
+    """Head step 2: only the first head of each pair sharing a KV head is
+    scheduled (one launch per pair of identical rows)."""
+    rng = np.random.default_rng(B * 700 + Hq + nQB)
+    sizes = rng.integers(0, 9, size=B * Hq * nQB)
+    row_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    order = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, head_step=2)
+    np.testing.assert_array_equal(order, sched_brute(row_ptr, B, Hq, Hkv, nQB, W, n_xcd, head_step=2))
+    heads = order // nQB % Hq
+    assert np.all(heads % 2 == 0) and len(set(order.tolist())) == B * Hq * nQB // 2
+    with pytest.raises(ValueError):   # three query heads per KV head do not pair up
+        oracle.schedule(row_ptr[:B * 3 * nQB + 1], B, 3, 1, nQB, W, n_xcd, head_step=2)
 
 
 def test_schedule_buckets_longest_first():
