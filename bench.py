@@ -270,12 +270,14 @@ def main():
         sys.exit(3)
 
 
-def attn_kernel_name(block, d):
+def attn_kernel_name(block, d, kv_share=False):
     """The attention kernel bsa_attn_fwd launches for dim-major V."""
+    if kv_share:
+        return "attn_ppg_128_%d" % d
     return ("attn_pp_128_%d" % d) if block == 128 else ("attn_dimv_%d_%d" % (block, d))
 
 
-ATTN_SOURCES = ("attn_pp.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip", "bsa_internal.h")
+ATTN_SOURCES = ("attn_pp.hip", "attn_ppg.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip", "bsa_internal.h")
 
 
 def attn_sources_sha256():
@@ -284,6 +286,15 @@ def attn_sources_sha256():
     for f in ATTN_SOURCES:
         h.update(open(os.path.join(ROOT, "block_sparse_attention_mask_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def kv_share_ok(dw, row_ptr, col, lw):
+    """Whether the query-head-pair kernel serves this workload: the shape
+    allows it and the pair check finds the rows identical."""
+    from block_sparse_attention_mask_amd import api, pipeline
+    if col is None or not pipeline.kv_share_supported(dw):
+        return False
+    return bool(api.pair_rows_equal(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, lw=lw).item())
 
 
 def attention_alone(dw, args, torch, crm=False):
@@ -304,12 +315,15 @@ def attention_alone(dw, args, torch, crm=False):
         pk = api.perm_from_labels(dw.labels_k, dw.n_clusters)
         k = api.permute_rows(dw.k, pk)
     v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd)
+    share = kv_share_ok(dw, row_ptr, col, lw) and not crm
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                         head_step=2 if share else 1)
     out = torch.empty((dw.B, dw.Hq, dw.N, dw.d), dtype=q.dtype, device=q.device)
 
     def launch():   # the query gather and the output scatter are fused into the kernel
         api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
-                     gather_perm_q=pq, causal=dw.causal, v_dim_major=True, out=out, crm=crm_rows)
+                     gather_perm_q=pq, causal=dw.causal, v_dim_major=True, out=out, crm=crm_rows,
+                     kv_share=share)
 
     for _ in range(10):
         launch()
@@ -699,11 +713,13 @@ def stage_times(pipeline, dw, args, torch):
     if api.spectral_supported(dw.nQB, dw.nQB):
         dec, _ = api.stage1_decide(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, dw.N, dw.d, dw.block, 10)
         row_perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, 10, enable=dec)
+    share = kv_share_ok(dw, row_ptr, col, lw)
     ev[3].record(s)
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm)
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm,
+                         head_step=2 if share else 1)
     ev[4].record(s)
     api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
-                 gather_perm_q=pq, causal=dw.causal, v_dim_major=True)
+                 gather_perm_q=pq, causal=dw.causal, v_dim_major=True, kv_share=share)
     ev[5].record(s)
     torch.cuda.synchronize()
     names = ["mask_to_csr", "perm_k_gather_and_v_transpose", "stage1_adaptive_skip", "schedule",
@@ -832,7 +848,8 @@ def workload_line(cfg, args, torch, with_oracle=True):
                       "block": w.block, "causal": bool(w.causal), "permuted": bool(w.permuted),
                       "log_weights": w.lw_map is not None},
             "nnz_blocks": nnz, "block_density": round(nnz / float(w.R * w.nKB), 5), "allowed_pairs": int(pairs),
-            "effective_gflop": round(flop / 1e9, 3), "kernel": attn_kernel_name(w.block, w.d),
+            "effective_gflop": round(flop / 1e9, 3), "kernel": attn_kernel_name(w.block, w.d, res.kv_share),
+            "kv_share": bool(res.kv_share),
             "kernel_alone_median50_ms": solo["median_ms"], "l2_flushed_ms": solo["flushed_ms"],
             "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "stage1_adaptive_skip": stage1_record(res)}

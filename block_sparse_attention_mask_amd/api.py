@@ -301,17 +301,39 @@ def transpose_rows(src: torch.Tensor, perm: Optional[torch.Tensor] = None, ld: O
 
 
 def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_rows: int = 0,
-             n_xcd: int = 8, order=None, stream=None, row_perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+             n_xcd: int = 8, order=None, stream=None, row_perm: Optional[torch.Tensor] = None,
+             head_step: int = 1) -> torch.Tensor:
+    """Launch order of the attention rows; head_step 2 lists one row per pair
+    of query heads sharing a KV head (for attn_fwd(kv_share=True))."""
     _dev(row_ptr, "row_ptr", torch.int32)
     if row_perm is not None:
         _dev(row_perm, "row_perm", torch.int32)
         if row_perm.numel() != B * Hq * nQB:
             raise ValueError("row_perm must hold B*Hq*nQB entries")
     if order is None:
-        order = torch.empty(B * Hq * nQB, dtype=torch.int32, device=row_ptr.device)
+        order = torch.empty(B * Hq * nQB // head_step, dtype=torch.int32, device=row_ptr.device)
     check("bsa_schedule", load().bsa_schedule(_ptr(row_ptr), B, Hq, Hkv, nQB, int(wave_rows), int(n_xcd),
-                                              _ptr(row_perm), _ptr(order), _stream(stream)))
+                                              _ptr(row_perm), int(head_step), _ptr(order), _stream(stream)))
     return order
+
+
+def pair_rows_equal(row_ptr: torch.Tensor, col: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int,
+                    lw: Optional[torch.Tensor] = None, equal: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Device int32 [1]: 1 if the rows of query heads 2j and 2j + 1 of every
+    KV group are identical (lists and log-weights), the precondition of
+    attn_fwd(kv_share=True); else 0."""
+    _dev(row_ptr, "row_ptr", torch.int32)
+    _dev(col, "col", torch.int32)
+    if lw is not None:
+        _dev(lw, "lw", torch.float32)
+    if row_ptr.numel() != B * Hq * nQB + 1:
+        raise ValueError("row_ptr must hold B*Hq*nQB + 1 entries")
+    if equal is None:
+        equal = torch.empty(1, dtype=torch.int32, device=row_ptr.device)
+    check("bsa_pair_rows_equal", load().bsa_pair_rows_equal(_ptr(row_ptr), _ptr(col), _ptr(lw), B, Hq, Hkv, nQB,
+                                                            _ptr(equal), _stream(stream)))
+    return equal
 
 
 def spectral_order(row_ptr: torch.Tensor, col: torch.Tensor, BH: int, nQB: int, nKB: int, iters: int = 10,
@@ -380,13 +402,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = False, scale: float = 0.0, causal: bool = False,
              v_dim_major: bool = False, crm: Optional[torch.Tensor] = None,
-             gather_perm_q: Optional[torch.Tensor] = None, stream=None):
+             gather_perm_q: Optional[torch.Tensor] = None, kv_share: bool = False, stream=None):
     """Block-sparse attention forward; returns (out, lse or None).  With
     ``v_dim_major`` v is [B][Hkv][d][ld] (keys contiguous, from transpose_rows),
     otherwise [B][Hkv][N][d].  With ``crm`` (CRM rows from crm_build) the lists
     come from the bitmask words and row_ptr/col may be None.  With
     ``gather_perm_q`` q is unpermuted and the kernel reads query row
-    gather_perm_q[bh][i] for permuted position i."""
+    gather_perm_q[bh][i] for permuted position i.  With ``kv_share`` the rows
+    of query heads 2j and 2j + 1 of every KV group must be identical
+    (pair_rows_equal checks it): one launch serves both, and order, if given,
+    comes from schedule(..., head_step=2)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     B, Hq, N, d = q.shape
@@ -413,6 +438,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
             raise ValueError("crm must hold B * Hq * ceil(N / block) rows")
     a.crm = _ptr(crm)
     a.gather_perm_q = _ptr(gather_perm_q)
+    a.kv_share = 2 if kv_share else 0
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse
 

@@ -127,5 +127,6 @@ constexpr int vm_lgkm0_wait_imm(int n) { return (n & 15) | (7 << 4) | (0 << 8) |
 hipError_t launch_attn_tokv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_pp(const AttnParams &p, int d, int64_t grid, hipStream_t s);
+hipError_t launch_attn_ppg(const AttnParams &p, int d, int64_t grid, hipStream_t s);
 
 }  // namespace bsa

@@ -1,5 +1,6 @@
 // bsa_attn_fwd: argument checks and dispatch to the attention kernels
-// (dim-major V: attn_pp.hip for 128-key blocks, attn_dimv.hip for 64;
+// (dim-major V: attn_pp.hip for 128-key blocks, attn_dimv.hip for 64, and
+// attn_ppg.hip for pairs of query heads that share K/V and their lists;
 // token-major V: attn_tokv.hip).  Lists come as CSR or as CRM rows; the
 // dim-major kernels have a variant for each.
 #include "attn_common.h"
@@ -45,8 +46,14 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   } else if (a->v_str[2] < a->d) {
     return BSA_ERR_ARG;
   }
-  const int64_t grid = a->order ? (a->n_order ? a->n_order : R) : R;
-  if (grid > R) return BSA_ERR_ARG;
+  if (a->kv_share != 0 && a->kv_share != 2) return BSA_ERR_ARG;
+  const int G = a->Hq / a->Hkv;
+  if (a->kv_share == 2 && (G % 2 || a->crm || a->v_layout != BSA_V_DIM_MAJOR || a->block != 128))
+    return BSA_ERR_UNSUPPORTED;
+  // with kv_share every launch serves a pair of rows
+  const int64_t rows = a->kv_share == 2 ? R / 2 : R;
+  const int64_t grid = a->order ? (a->n_order ? a->n_order : rows) : rows;
+  if (grid > rows) return BSA_ERR_ARG;
   if (grid == 0) return BSA_OK;
 
   bsa::AttnParams p;
@@ -71,7 +78,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   p.N = a->N;
   p.R = R;
   p.Hq = a->Hq;
-  p.G = a->Hq / a->Hkv;
+  p.G = G;
   p.nQB = (int)nQB;
   p.causal = a->causal ? 1 : 0;
   const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->d);
@@ -80,6 +87,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   hipStream_t s = bsa_hip_stream(stream);
   hipError_t err;
   if (a->v_layout == BSA_V_TOKEN_MAJOR) err = bsa::launch_attn_tokv(p, a->block, a->d, grid, s);
+  else if (a->kv_share == 2) err = bsa::launch_attn_ppg(p, a->d, grid, s);
   else if (a->block == 128) err = bsa::launch_attn_pp(p, a->d, grid, s);
   else err = bsa::launch_attn_dimv(p, a->block, a->d, grid, s);
   return err == hipSuccess ? BSA_OK : BSA_ERR_HIP;

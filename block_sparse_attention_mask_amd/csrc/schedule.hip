@@ -17,8 +17,16 @@
 // A stage-1 order (WaveAlign section IV-C, bsa_spectral_order) may replace
 // the query-block order within each head before the buckets are formed.
 //
+// With a head step of 2 only the first head of each pair of query heads that
+// share a KV head is scheduled: the attention kernel that serves both heads'
+// (identical) rows in one launch reads this table.
+//
 // One workgroup per bucket: keys (INT32_MAX - nnz) << 32 | position are
 // sorted ascending with a bitonic network in LDS.
+//
+// bsa_pair_rows_equal checks the precondition of that pair kernel: one
+// wavefront per pair of rows compares lengths, block indices and log-weight
+// bits, and clears a flag on any difference.
 #include "bsa_internal.h"
 
 namespace {
@@ -28,10 +36,10 @@ constexpr int kMaxWave = 2048;
 __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ row_ptr, int Hq,
                                                         int Hkv, int nQB, int W, int n_xcd,
                                                         int64_t R, const int32_t *__restrict__ row_perm,
-                                                        int32_t *__restrict__ order) {
+                                                        int hs, int32_t *__restrict__ order) {
   __shared__ uint64_t key[kMaxWave];
-  const int G = Hq / Hkv;
-  const int64_t seg = (int64_t)G * nQB;
+  const int G = Hq / Hkv, Gs = G / hs;   // scheduled heads per KV head: every hs-th
+  const int64_t seg = (int64_t)Gs * nQB;
   const int64_t nbk = (seg + W - 1) / W;           // buckets per (b, g) segment
   const int64_t s = blockIdx.x / nbk, k = blockIdx.x % nbk;
   const int64_t start = s * seg + k * W;           // logical position of the bucket's first row
@@ -39,10 +47,10 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   int P2 = 1;
   while (P2 < n) P2 <<= 1;
   const int64_t b = s / Hkv, g = s % Hkv;
-  // row at segment position j: head (b, g G + j % G), query block j / G (or
-  // its stage-1 replacement); -1 for a corrupt stage-1 entry
+  // row at segment position j: head (b, g G + hs (j % Gs)), query block
+  // j / Gs (or its stage-1 replacement); -1 for a corrupt stage-1 entry
   auto row_at = [&](int64_t j) -> int64_t {
-    const int64_t p = j / G, h = b * Hq + g * G + j % G;
+    const int64_t p = j / Gs, h = b * Hq + g * G + hs * (j % Gs);
     const int64_t u = row_perm ? (int64_t)row_perm[h * nQB + p] : p;
     return (u >= 0 && u < nQB) ? h * nQB + u : -1;
   };
@@ -91,25 +99,62 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   }
 }
 
+__global__ void flag_set_kernel(int32_t *__restrict__ flag) {
+  if (threadIdx.x == 0) flag[0] = 1;
+}
+
+__global__ __launch_bounds__(64) void pair_rows_equal_kernel(const int32_t *__restrict__ row_ptr,
+                                                             const int32_t *__restrict__ col,
+                                                             const float *__restrict__ lw, int nQB,
+                                                             int32_t *__restrict__ equal) {
+  const int64_t q = blockIdx.x, pr = q / nQB, u = q - pr * nQB;
+  const int64_t r0 = 2 * pr * nQB + u, r1 = r0 + nQB;   // (b, 2j, u) and (b, 2j + 1, u)
+  const int32_t a0 = row_ptr[r0], a1 = row_ptr[r0 + 1], b0 = row_ptr[r1], b1 = row_ptr[r1 + 1];
+  bool diff = a1 - a0 != b1 - b0;
+  if (!diff)
+    for (int32_t i = threadIdx.x; i < a1 - a0; i += 64) {
+      diff = diff || col[a0 + i] != col[b0 + i];
+      if (lw) diff = diff || __float_as_uint(lw[a0 + i]) != __float_as_uint(lw[b0 + i]);
+    }
+  if (diff) equal[0] = 0;
+}
+
 }  // namespace
 
+extern "C" int bsa_pair_rows_equal(const int32_t *row_ptr, const int32_t *col, const float *lw, int32_t B,
+                                   int32_t Hq, int32_t Hkv, int32_t nQB, int32_t *equal, bsa_stream_t stream) {
+  if (!row_ptr || !col || !equal || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
+  if (Hq % Hkv) return BSA_ERR_ARG;
+  if ((Hq / Hkv) % 2) return BSA_ERR_UNSUPPORTED;
+  const int64_t pairs = (int64_t)B * (Hq / 2) * nQB;
+  if (2 * pairs >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  hipStream_t s = bsa_hip_stream(stream);
+  hipLaunchKernelGGL(flag_set_kernel, dim3(1), dim3(64), 0, s, equal);
+  BSA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(pair_rows_equal_kernel, dim3((unsigned)pairs), dim3(64), 0, s, row_ptr, col, lw, nQB, equal);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}
+
 extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
-                            int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm, int32_t *order,
-                            bsa_stream_t stream) {
+                            int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm, int32_t head_step,
+                            int32_t *order, bsa_stream_t stream) {
   if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
   if (Hq % Hkv) return BSA_ERR_ARG;
+  if (head_step != 1 && head_step != 2) return BSA_ERR_ARG;
+  if ((Hq / Hkv) % head_step) return BSA_ERR_ARG;
   if (wave_rows < 0 || n_xcd < 0 || n_xcd > 64) return BSA_ERR_ARG;
   if (wave_rows > kMaxWave) return BSA_ERR_UNSUPPORTED;
-  const int64_t R = (int64_t)B * Hq * nQB;
-  if (R >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  const int64_t R = (int64_t)B * Hq * nQB / head_step;   // rows scheduled
+  if ((int64_t)B * Hq * nQB >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
   // wave_rows = 0: one bucket per KV-group segment (up to 2048 rows), i.e. the
   // whole head longest-first, which measured fastest on MI355X together with
   // the XCD-contiguous deal
   const int W = wave_rows ? wave_rows : kMaxWave;
-  const int64_t seg = (int64_t)(Hq / Hkv) * nQB;
+  const int64_t seg = (int64_t)(Hq / Hkv / head_step) * nQB;
   const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),
-                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, row_perm, order);
+                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, row_perm, head_step, order);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

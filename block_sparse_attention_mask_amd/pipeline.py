@@ -89,6 +89,7 @@ class StepResult:
     crm: Optional[torch.Tensor] = None
     stage1_decision: Optional[torch.Tensor] = None   # device int32 [1] (adaptive skip)
     stage1_stats: Optional[torch.Tensor] = None      # device float64 [7]
+    kv_share: bool = False                            # query-head pairs served in one launch
 
 
 def _stage1_order(dw: DeviceWorkload, row_ptr, col, stage1: str, iters: int, stream):
@@ -111,11 +112,31 @@ def _stage1_order(dw: DeviceWorkload, row_ptr, col, stage1: str, iters: int, str
     return perm, dec, stats
 
 
+def kv_share_supported(dw: DeviceWorkload, v_dim_major: bool = True) -> bool:
+    """Whether the shape allows the query-head-pair path: an even number of
+    query heads per KV head, 128-token blocks, dim-major V."""
+    return (dw.Hq // dw.Hkv) % 2 == 0 and dw.block == 128 and v_dim_major
+
+
+def _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, stream) -> bool:
+    if kv_share is False:
+        return False
+    if kv_share not in (True, "auto"):
+        raise ValueError("kv_share must be True, False or 'auto'")
+    if not kv_share_supported(dw, v_dim_major):
+        if kv_share is True:
+            raise ValueError("kv_share needs Hq/Hkv even, 128-token blocks and dim-major V")
+        return False
+    if kv_share is True:
+        return True   # the caller vouches for identical rows
+    return bool(api.pair_rows_equal(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, lw=lw, stream=stream).item())
+
+
 def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows: int = 0,
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
             v_dim_major: bool = True, stream=None, stage1: str = "auto", stage1_iters: int = 10,
             crm: bool = False, sampler: Optional[dict] = None, fuse_gather: bool = True,
-            overlap: bool = False) -> StepResult:
+            overlap: bool = False, kv_share="auto") -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  ``stage1``
     selects WaveAlign's stage 1 in front of the schedule: "auto" (the
@@ -131,14 +152,17 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     ``sampler`` = {"m_exact": E, "m_sample": S, "uoff": float64 [B*Hq][G]}
     (a permuted workload) the block mask and log-weights come from the
     group-shared importance sampler over the permuted Q and K instead of
-    the workload's mask."""
+    the workload's mask.  ``kv_share`` (True, False or "auto"): serve the
+    identical rows of query-head pairs sharing a KV head in one launch (K/V
+    tiles staged once for both heads); "auto" checks the rows on the device
+    and uses it where they are identical and the shape allows it."""
     crm_rows = None
     if sampler is not None:
         return _forward_sampled(dw, sampler, schedule, n_xcd, wave_rows, fuse_scatter, want_lse, attn_events,
                                 stream, stage1, stage1_iters)
     if overlap and not crm:
         return _forward_overlapped(dw, schedule, n_xcd, wave_rows, fuse_scatter, fuse_gather, want_lse,
-                                   attn_events, v_dim_major, stream, stage1, stage1_iters)
+                                   attn_events, v_dim_major, stream, stage1, stage1_iters, kv_share)
     if crm:
         if dw.lw_map is not None or not v_dim_major:
             raise ValueError("CRM lists carry no log-weights and need dim-major V")
@@ -160,17 +184,18 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             v = api.permute_rows(dw.v, perm_k, stream=stream)
     if v_dim_major:
         v = api.transpose_rows(dw.v, perm_k, ld=dw.nQB * dw.block, stream=stream)
-    order = dec = stats = None
+    order = dec = stats = row_perm = None
     if schedule:
-        row_perm = None
         if crm and stage1 == "on":
             _, nnz = api.crm_row_ptr(crm_rows, dw.nQB, row_ptr=row_ptr, stream=stream)
             cols = api.crm_to_csr(crm_rows, dw.nQB, row_ptr, nnz, stream=stream)
             row_perm, _, _ = _stage1_order(dw, row_ptr, cols, "on", stage1_iters, stream)
         elif not crm:
             row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
+    share = False if crm else _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, stream)
+    if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
-                             row_perm=row_perm)
+                             row_perm=row_perm, head_step=2 if share else 1)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
@@ -178,7 +203,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     gperm = perm_q if (dw.permuted and fuse_gather) else None
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
                             want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, crm=crm_rows,
-                            gather_perm_q=gperm, stream=stream)
+                            gather_perm_q=gperm, kv_share=share, stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if dw.permuted and not fuse_scatter:
@@ -187,7 +212,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows, dec, stats)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows, dec, stats, share)
 
 
 def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: int, wave_rows: int,
@@ -233,11 +258,13 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
 
 def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_rows: int, fuse_scatter: bool,
                         fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream, stage1: str,
-                        stage1_iters: int) -> StepResult:
+                        stage1_iters: int, kv_share="auto") -> StepResult:
     """The same step with two streams: [key labels -> perm_k, K gather, V
     gather + transpose] on a side stream beside [query labels -> perm_q,
     mask -> CSR without a host round trip, schedule] on the caller's stream;
-    attention waits for both."""
+    attention waits for both.  kv_share="auto" reads the pair check's flag
+    on the host (the one round trip of this path, taken only on shapes the
+    pair kernel serves)."""
     main = stream if stream is not None else torch.cuda.current_stream()
     side = _side_stream(dw.q.device)
     side.wait_stream(main)
@@ -262,8 +289,10 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
     order = dec = stats = None
     if schedule:
         row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, main)
+    share = _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, main)
+    if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main,
-                             row_perm=row_perm)
+                             row_perm=row_perm, head_step=2 if share else 1)
     main.wait_stream(side)
     for t in (perm_k, k, v):
         if t is not None:
@@ -274,7 +303,7 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
         attn_events[0].record(main)
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
                             want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major,
-                            gather_perm_q=gperm, stream=main)
+                            gather_perm_q=gperm, kv_share=share, stream=main)
     if attn_events is not None:
         attn_events[1].record(main)
     if dw.permuted and not fuse_scatter:
@@ -283,4 +312,4 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats, share)

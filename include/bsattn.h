@@ -341,12 +341,18 @@ int bsa_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_ptr
  * the list is dealt to launch indices so that the GPU's round-robin dispatch
  * gives XCD x the x-th contiguous slice:
  * order[i] = logical[start(i % n_xcd) + i / n_xcd].  wave_rows = 0 selects
- * 2048 (a whole segment of up to 2048 rows is one bucket).  row_ptr: device
- * int32 [R+1]; order: device int32 [R] (output).  wave_rows <= 2048.
- * Asynchronous.
+ * 2048 (a whole segment of up to 2048 rows is one bucket).  head_step 1
+ * schedules every row; head_step 2 only the rows of the first head of each
+ * pair of query heads sharing a KV head (heads g*G + 2j), for the attention
+ * path that serves a pair's identical rows in one launch (kv_share), and
+ * needs G even.  row_ptr: device int32 [B*Hq*nQB + 1]; order: device int32
+ * [B*Hq*nQB / head_step] (output).  wave_rows <= 2048.  BSA_ERR_ARG for
+ * NULL pointers, non-positive sizes, Hq % Hkv != 0, head_step not 1 or 2 or
+ * not dividing G.  Asynchronous.
  * ------------------------------------------------------------------------- */
 int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB, int32_t wave_rows,
-                 int32_t n_xcd, const int32_t *row_perm, int32_t *order, bsa_stream_t stream);
+                 int32_t n_xcd, const int32_t *row_perm, int32_t head_step, int32_t *order,
+                 bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Block-sparse attention forward.
@@ -384,6 +390,18 @@ int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int
  * section 7.3) and row_ptr/col are not read (may be NULL); it requires
  * v_layout = BSA_V_DIM_MAJOR and lw = NULL (else BSA_ERR_UNSUPPORTED).
  * Results are bit-identical to the CSR lists the same mask gives.
+ * kv_share: 0, or 2 when query heads 2j and 2j + 1 of every KV-head group
+ * have identical rows (same lists, same log-weights; grouped-query
+ * attention whose block pattern is shared by the group's heads, e.g. the
+ * Scatter/Gather prefill patterns of INTRA, section 4).  Then one launch
+ * serves both rows of a pair, staging each K/V tile once for both heads; the
+ * rows of head 2j + 1 are not read, and bsa_pair_rows_equal checks the
+ * precondition.  Requires G = Hq / Hkv even, v_layout = BSA_V_DIM_MAJOR,
+ * block = 128 and crm = NULL (else BSA_ERR_UNSUPPORTED); order then lists
+ * rows of even heads only (bsa_schedule with head_step 2; other entries
+ * compute nothing), n_order <= R / 2, and without order launch i serves the
+ * i-th row of an even head.  Results equal those of kv_share = 0 on rows
+ * that meet the precondition.
  * Asynchronous.
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -403,9 +421,24 @@ typedef struct {
   int32_t v_layout; /* BSA_V_TOKEN_MAJOR or BSA_V_DIM_MAJOR */
   const uint32_t *crm; /* CRM rows in place of row_ptr/col, or NULL */
   const int32_t *gather_perm_q; /* query gather (int32 [B*Hq][N]), or NULL */
+  int32_t kv_share; /* 0, or 2: rows of heads 2j and 2j + 1 of a KV group are identical */
 } bsa_attn_args;
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Precondition check of bsa_attn_fwd's kv_share = 2: whether every pair of
+ * query heads 2j, 2j + 1 within a KV-head group has identical rows, i.e.
+ * for every b, even h and query block u the rows (b, h, u) and (b, h + 1, u)
+ * list the same blocks in the same order with the same log-weights (bit
+ * for bit; lw optional).  row_ptr: device int32 [B*Hq*nQB + 1]; col, lw:
+ * device, as bsa_csr_fill writes them; equal: device int32 [1] (output, 1
+ * if every pair is identical, else 0).  BSA_ERR_ARG for NULL pointers,
+ * non-positive sizes, Hq % Hkv != 0; BSA_ERR_UNSUPPORTED when G = Hq / Hkv
+ * is odd.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_pair_rows_equal(const int32_t *row_ptr, const int32_t *col, const float *lw, int32_t B, int32_t Hq,
+                        int32_t Hkv, int32_t nQB, int32_t *equal, bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Token-level attention over computational query sets.

@@ -82,10 +82,23 @@ def test_perm_argument_errors(L):
 
 
 def test_schedule_argument_errors(L):
-    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, None, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, 1, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 16, 8, None, 3, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 1
+    assert L.bsa_schedule(FAKE, 1, 6, 2, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 3
+
+
+def test_pair_rows_equal_argument_errors(L):
+    f = L.bsa_pair_rows_equal
+    assert f(None, FAKE, None, 1, 4, 2, 8, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, None, None, 1, 4, 2, 8, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, FAKE, None, 1, 4, 2, 8, None, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, FAKE, None, 1, 4, 2, 0, FAKE, None) == _lib.BSA_ERR_ARG
+    assert f(FAKE, FAKE, None, 1, 6, 4, 8, FAKE, None) == _lib.BSA_ERR_ARG            # Hq % Hkv
+    assert f(FAKE, FAKE, None, 1, 6, 2, 8, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED    # G = 3
 
 
 def test_spectral_order_argument_errors(L):
@@ -261,6 +274,14 @@ def _args(**kw):
      _lib.BSA_ERR_UNSUPPORTED),                                                              # CRM has no weights
     (dict(crm=FAKE), _lib.BSA_ERR_UNSUPPORTED),                                              # CRM: dim-major V only
     (dict(crm=None, col=None), _lib.BSA_ERR_ARG),
+    (dict(kv_share=1), _lib.BSA_ERR_ARG),
+    (dict(kv_share=2, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), Hkv=4),
+     _lib.BSA_ERR_UNSUPPORTED),                                                              # G = 1: no pairs
+    (dict(kv_share=2), _lib.BSA_ERR_UNSUPPORTED),                                            # token-major V
+    (dict(kv_share=2, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), block=64),
+     _lib.BSA_ERR_UNSUPPORTED),
+    (dict(kv_share=2, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), order=FAKE, n_order=17),
+     _lib.BSA_ERR_ARG),                                                                      # > R / 2 launches
 ])
 def test_attn_argument_errors(L, kw, code):
     a = _args(**kw)
