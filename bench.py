@@ -436,16 +436,16 @@ def token_set_stage(torch):
         f = lambda H: torch.randn((1, H, N, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
         return f(Hq), f(Hkv), f(Hkv)
 
-    def timed(name, shape, q, k, v, q_idx, kv_ptr, kv_idx, causal, pairs):
+    def timed(name, shape, q, k, v, q_idx, kv_ptr, kv_idx, causal, pairs, kv_share=False):
         out = torch.empty_like(q)
         for _ in range(3):
-            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal)
+            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal, kv_share=kv_share)
         s = torch.cuda.current_stream()
         ms = []
         for _ in range(10):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(s)
-            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal)
+            api.attn_tok_fwd(q, k, v, q_idx, kv_ptr, kv_idx, out=out, causal=causal, kv_share=kv_share)
             b.record(s)
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
@@ -463,6 +463,10 @@ def token_set_stage(torch):
     qkv_s = qkv(Hq, Hkv, N)
     timed("intra_scatter_llama3_8b_32k", "1x32q/8kv x 32768, d128, 8 groups, causal, 64-query sets",
           *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
+    # the same sets served per pair of query heads of a KV group (the map is
+    # the same for every head): each gathered K/V tile serves both heads
+    timed("intra_scatter_llama3_8b_32k_head_pairs", "same, one launch per pair of query heads sharing a KV head",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=True)
     # the same pattern executed as 128-query sets (two consecutive 64-query
     # sets of a group share the later one's key list; causal masking keeps
     # the computation identical)
@@ -473,6 +477,8 @@ def token_set_stage(torch):
     maps = synth.cqs_per_head(synth.cqs_gather1(N, R, 64, True), Hq)
     timed("intra_gather1_llama3_8b_32k", "1x32q/8kv x 32768, d128, 8 groups of cyclic 8-token segments, causal, "
           "64-query sets", *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
+    timed("intra_gather1_llama3_8b_32k_head_pairs", "same, one launch per pair of query heads sharing a KV head",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=True)
     del qkv_s
     # INTRA Gather 0, FLUX.1-dev 2048x2048 image (128x128 tokens): 8x8 patches, 16x16 windows
     H = W = 128

@@ -61,6 +61,7 @@ class TokArgs(ctypes.Structure):
         ("q_idx", P), ("kv_ptr", P), ("kv_idx", P),
         ("scale", ctypes.c_float),
         ("causal", I32),
+        ("kv_share", I32),
     ]
 
 

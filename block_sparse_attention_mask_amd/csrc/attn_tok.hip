@@ -10,12 +10,19 @@
 // sequence and, when causal, keys s_e > t do not take part.  Outputs go back
 // to the query positions (INTRA, section 4.8).
 //
-// Mapping to the hardware (one workgroup per set, BQ = 64 or 128 queries,
-// head dim 128, 64-key tiles):
-//   * 2 BQ / 32 wavefronts, two per SIMD: wavefront w owns the 32 queries of
-//     group w % (BQ/32) and the key half w / (BQ/32) (keys 0-31 or 32-63 of
-//     every tile), with its own online-softmax state; the halves merge once
-//     through LDS at the end.
+// Mapping to the hardware (one workgroup per set, or per pair of sets of
+// the two query heads 2j, 2j + 1 of a KV group when their query slots and
+// key lists are identical; BQ = 64 or 128 queries, head dim 128, 64-key
+// tiles; four wavefronts, two workgroups per CU):
+//   * 64-query sets of one head: wavefront w owns the 32 queries of group
+//     w % 2 and the key half w / 2 (keys 0-31 or 32-63 of every tile), with
+//     its own online-softmax state; the halves merge once through LDS at the
+//     end.
+//   * 128-query sets, and pairs of 64-query sets: wavefront w owns 32
+//     queries (query group, or head and query group) and every key of every
+//     tile (two 32-key M tiles per step), so no merge is needed.  With two
+//     heads every gathered tile serves both, halving the gather traffic per
+//     unit of work.
 //   * The selected K and V rows are gathered straight into LDS by
 //     buffer_load_dwordx4 ... lds: each lane copies one 16-byte chunk of one
 //     key row, with the row's position taken from the staged key list, so a
@@ -32,11 +39,14 @@
 //     sequence, or after the set's first query when causal) are flagged
 //     while the list is staged; only those tiles read key positions per
 //     score.
-//   * Software pipeline as in the 64-key block kernel: S(i+1) = K(i+1) Q^T in
-//     the same basic block as the exponentials of S(i), then O += V(i) P(i);
-//     K and V tiles rotate through two LDS stages each.
+//   * Software pipeline over two stages of K and of V: interval i computes
+//     S(i+1) = K(i+1) Q^T in the same basic block as the exponentials of
+//     S(i), then O += V(i) P(i), while the gathers of K(i+2) and V(i+1) are
+//     in flight.
 //   * Softmax in base 2, fp32; the running max is raised (and O rescaled)
 //     only when a tile's max exceeds it by more than 8.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace bsa {
@@ -45,22 +55,26 @@ namespace tok {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int BQ>
+template <int BQ, int HP, int KSPLIT>
 struct TCfg {
   static constexpr int D = 128;
-  static constexpr int NQG = BQ / 32;             // query groups
-  static constexpr int NW = 2 * NQG;              // wavefronts: query group x key half
+  static constexpr int NQG = BQ / 32;             // query groups per head
+  static constexpr int NG = HP * NQG;             // (head, query group) pairs
+  static constexpr int NW = KSPLIT * NG;          // wavefronts: pair x key part
   static constexpr int NT = 64 * NW;              // threads
   static constexpr int BK = 64;                   // keys per tile
+  static constexpr int MTW = 2 / KSPLIT;          // 32-key M tiles of a tile per wavefront
   static constexpr int KS = D / 16;               // k-steps of K Q^T
   static constexpr int DT = D / 32;               // 32-dim M tiles of O^T
   static constexpr int TILE = BK * D * 2;         // bytes of a K or V tile
   static constexpr int NCOPY = TILE / 1024;       // 1 KB copies per tile (4 rows each)
   static constexpr int NC = NCOPY / NW;           // copies per wavefront per tile
-  static constexpr int LIST = 1024;               // list entries staged at a time
+  static constexpr int LIST = 2048;               // list entries staged at a time
   static constexpr int NTL = LIST / BK;           // tiles per staged chunk
+  static_assert(KSPLIT == 1 || KSPLIT == 2, "whole tiles or key halves");
   static_assert(NCOPY % NW == 0, "whole copies per wavefront");
-  static_assert(64 * DT * 16 * 4 <= TILE, "merge data of a query group fits a tile stage");
+  static_assert(KSPLIT == 1 || NG <= 4, "merge data of every (head, query group) fits a tile buffer");
+  static_assert(64 * DT * 16 * 4 <= TILE, "merge data of a query group fits a tile buffer");
 };
 
 struct TokParams {
@@ -76,41 +90,53 @@ struct TokParams {
 
 __device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 3) & 1); }
 
-template <int BQ>
+template <int BQ, int HP, int KSPLIT>
 __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
-  using C = TCfg<BQ>;
-  constexpr int D = C::D;
-  __shared__ __attribute__((aligned(1024))) uint8_t k0[C::TILE], k1[C::TILE], v0[C::TILE], v1[C::TILE];
+  using C = TCfg<BQ, HP, KSPLIT>;
+  constexpr int D = C::D, MTW = C::MTW;
+  // tile buffers K0, K1, V0, V1 (index 0-3), each C::TILE bytes
+  __shared__ __attribute__((aligned(1024))) uint8_t stg[4][C::TILE];
+  uint8_t *const k0 = stg[0], *const k1 = stg[1], *const v0 = stg[2], *const v1 = stg[3];
   __shared__ int32_t lcol[C::LIST];
   __shared__ int32_t tflag[C::NTL];
   __shared__ int32_t qmin_s;
-  __shared__ float mrg_ml[C::NQG][2][64];
+  __shared__ float mrg_ml[KSPLIT == 2 ? C::NG : 1][2][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < C::NW);
   const int ln = lane & 31, hf = lane >> 5;
-  const int qg = wave % C::NQG, kh = wave / C::NQG;
-  const int64_t set = blockIdx.x;
-  if (set >= p.n_sets) return;
-  const int64_t bh = set / p.sets;
-  const int64_t b = bh / p.Hq;
-  const int h = (int)(bh - b * p.Hq);
+  const int gi = wave % C::NG, kh = wave / C::NG;   // (head, query group) pair, key half
+  const int hd = gi / C::NQG, qg = gi % C::NQG;
+  // the set whose slots and list this workgroup reads: set i, or with two
+  // heads the i-th set of an even head (its partner head's set is identical)
+  // (set counts are below 2^31: 32-bit index arithmetic)
+  int set0;
+  if (HP == 1) {
+    set0 = (int)blockIdx.x;
+  } else {
+    const int i = (int)blockIdx.x, pr = i / p.sets;
+    set0 = (2 * pr) * p.sets + (i - pr * p.sets);
+  }
+  if (set0 >= p.n_sets) return;
+  const int bh = set0 / p.sets + hd;   // this wavefront's head
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
   const int g = h / p.G;
   const int N = p.N;
-  const int e0 = p.kv_ptr[set], e1 = p.kv_ptr[set + 1];
+  const int e0 = p.kv_ptr[set0], e1 = p.kv_ptr[set0 + 1];
 
   // this lane's query and the set's first query (for the causal flags)
-  const int32_t qraw = p.q_idx[set * BQ + qg * 32 + ln];
+  const int32_t qraw = p.q_idx[(int64_t)set0 * BQ + qg * 32 + ln];
   const bool qok = qraw >= 0 && qraw < N;
   const int qi = qok ? qraw : -1;
   if (tid == 0) qmin_s = 0x7fffffff;
   __syncthreads();
-  if (kh == 0 && qok) atomicMin(&qmin_s, qi);
+  if (kh == 0 && hd == 0 && qok) atomicMin(&qmin_s, qi);
 
   const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((int64_t)(N - 1) * p.qs2 + D) * 2);
-  const rsrc_t krs = make_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
-  const rsrc_t vrs = make_rsrc(p.v + b * p.vs0 + g * p.vs1, ((int64_t)(N - 1) * p.vs2 + D) * 2);
+  const i32x4 krs = buffer_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
+  const i32x4 vrs = buffer_rsrc(p.v + b * p.vs0 + g * p.vs1, ((int64_t)(N - 1) * p.vs2 + D) * 2);
   const uint32_t ks2b = (uint32_t)p.ks2 * 2, vs2b = (uint32_t)p.vs2 * 2;
 
   // Q^T fragment (B operand): lane (ln, hf) holds q[qi][16 ks + 8 hf .. +7]
@@ -123,29 +149,46 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
 
   // Copies: copy I (0..NCOPY-1) of a tile fills LDS bytes [1024 I, 1024 I + 1024)
   // of its stage, rows 4 I .. 4 I + 3; lane l writes row 4 I + l / 16 at chunk
-  // position l % 16, which holds source chunk position ^ swizzle(row).
+  // position l % 16, which holds source chunk position ^ swizzle(row).  Tile
+  // indices past the staged list read zeros.
+  // Every copy's LDS address is this wavefront's base plus a compile-time
+  // offset (buffer BUF, slot t).
   const int crow = lane >> 4, cpos = lane & 15;
+  const uint32_t wbase =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)&stg[0][0] + (uint32_t)wave * 1024u;
   int n = 0;   // entries of the staged chunk
-  auto issue = [&](int i, uint8_t *dst, bool is_v) {
-#pragma unroll
-    for (int t = 0; t < C::NC; ++t) {
-      const int I = wave + C::NW * t;
-      const int row = 4 * I + crow;
+  auto issue = [&](int i, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;   // 0, 1: K buffers; 2, 3: V buffers
+    static_for<0, C::NC>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      const int row = 4 * (wave + C::NW * t) + crow;
       const int li = i * C::BK + row;
       const int kp = li < n ? lcol[li] : -1;
       const bool ok = kp >= 0 && kp < N;
-      uint32_t off;
-      if (is_v) off = ok ? (uint32_t)kp * vs2b + ((cpos ^ vswz(row)) << 4) : kOOR;
-      else off = ok ? (uint32_t)kp * ks2b + ((cpos ^ (row & 15)) << 4) : kOOR;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_v ? vrs : krs, (lds_void *)(dst + 1024 * I), 16, off, 0, 0, 0);
-    }
+      if constexpr (BUF >= 2) {
+        const uint32_t off = ok ? (uint32_t)kp * vs2b + ((cpos ^ vswz(row)) << 4) : kOOR;
+        lds_copy16_at<(uint32_t)(BUF * C::TILE + 1024 * C::NW * t)>(vrs, wbase, off, 0u);
+      } else {
+        const uint32_t off = ok ? (uint32_t)kp * ks2b + ((cpos ^ (row & 15)) << 4) : kOOR;
+        lds_copy16_at<(uint32_t)(BUF * C::TILE + 1024 * C::NW * t)>(krs, wbase, off, 0u);
+      }
+    });
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
 
-  // K reads: this lane's score row is key 32 kh + key_of_row(ln) of the tile;
+  // This wavefront's keys of a tile: M tiles kh MTW + jj (32 keys each).  K
+  // reads: the lane's score row of M tile t is key 32 t + key_of_row(ln);
   // chunk 2 ks + hf sits at (2 ks) ^ (hf ^ (key mod 16))
-  const int kkey = 32 * kh + key_of_row(ln);
-  const int kbase = kkey * (D * 2);
-  const int kx = hf ^ (kkey & 15);
+  int kbase[MTW], kx[MTW];
+#pragma unroll
+  for (int jj = 0; jj < MTW; ++jj) {
+    const int kkey = 32 * (kh * MTW + jj) + key_of_row(ln);
+    kbase[jj] = kkey * (D * 2);
+    kx[jj] = hf ^ (kkey & 15);
+  }
   // V transpose reads: lane (gg = lane / 16, j = lane / 4 mod 4, qq = lane mod 4)
   // supplies the address of keys kb0 + 8 (gg / 2) + j (+4 for the second read),
   // dims 32 dt + 16 (gg mod 2) + 4 qq .. +3
@@ -154,14 +197,18 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   const int vcc = (2 * (gg & 1) + (qq >> 1)) ^ (2 * (gg >> 1));   // low two bits of the chunk position
   const int vhalf = (qq & 1) * 8;
 
-  auto qk = [&](f32x16 &s, const uint8_t *kt) {
+  auto qk = [&](f32x16 (&s)[MTW], const uint8_t *kt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int jj = 0; jj < MTW; ++jj)
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(kt + kbase + (((2 * ks) ^ kx) << 4));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s, 0, 0, 0);
-    }
+      for (int i = 0; i < 16; ++i) s[jj][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < MTW; ++jj) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(kt + kbase[jj] + (((2 * ks) ^ kx[jj]) << 4));
+        s[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[jj], 0, 0, 0);
+      }
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -170,22 +217,25 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  f32x16 sa, sb;
-  const int ob = 32 * kh + 8 * hf;   // tile key of this lane's first score row
+  f32x16 sa[MTW], sb[MTW];
 
-  auto interval = [&](int i, f32x16 &sc, f32x16 &sn, const uint8_t *kt_next, const uint8_t *vt) {
+  auto interval = [&](int i, f32x16 (&sc)[MTW], f32x16 (&sn)[MTW], const uint8_t *kt_next, const uint8_t *vt) {
     if (tflag[i]) {
-      // element e holds tile key ob + 16 (e >> 3) + (e & 7)
+      // element e of M tile t holds tile key 32 t + 8 hf + 16 (e >> 3) + (e & 7)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int li = i * C::BK + ob + 16 * (e >> 3) + (e & 7);
-        const int kp = li < n ? lcol[li] : -1;
-        if (kp < 0 || kp >= N || (p.causal && kp > qi)) sc[e] = -INFINITY;
-      }
+      for (int jj = 0; jj < MTW; ++jj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int li = i * C::BK + 32 * (kh * MTW + jj) + 8 * hf + 16 * (e >> 3) + (e & 7);
+          const int kp = li < n ? lcol[li] : -1;
+          if (kp < 0 || kp >= N || (p.causal && kp > qi)) sc[jj][e] = -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    for (int jj = 0; jj < MTW; ++jj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[jj][e]);
     mx = halves_max(mx);
     const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * p.c;
     if (__any(m_tile > m_run + kTau)) {
@@ -199,36 +249,40 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
       m_run = m_new;
     }
     const float nb = -(m_run == -INFINITY ? 0.f : m_run);
-    bf16x8 pb[2];
+    bf16x8 pb[MTW][2];
     auto exps = [&]() {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float pv[8];
+      for (int jj = 0; jj < MTW; ++jj)
 #pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(sc[8 * s2 + e8], p.c, nb));
-        l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        pb[s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                                                       cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
-      }
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float pv[8];
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) pv[e8] = __builtin_amdgcn_exp2f(fmaf(sc[jj][8 * s2 + e8], p.c, nb));
+          l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+          pb[jj][s2] = __builtin_bit_cast(bf16x8, make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                                                             cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7])));
+        }
     };
     // S(i+1) is computed unconditionally so that the MFMAs and the
     // exponentials share one basic block; after the last tile it reads a
-    // stale stage and is never used
+    // stage of zeros or a stale one and is never used
     qk(sn, kt_next);
     exps();
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int r0 = 32 * kh + 16 * s2 + vrow0;   // keys of the first transpose read
+    for (int jj = 0; jj < MTW; ++jj)
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int pos = (4 * (dt ^ vj)) | vcc;
-        const uint8_t *a0 = vt + r0 * (D * 2) + (pos << 4) + vhalf;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a0));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a0 + 4 * (D * 2)));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], o[dt], 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int r0 = 32 * (kh * MTW + jj) + 16 * s2 + vrow0;   // keys of the first transpose read
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const int pos = (4 * (dt ^ vj)) | vcc;
+          const uint8_t *a0 = vt + r0 * (D * 2) + (pos << 4) + vhalf;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a0));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a0 + 4 * (D * 2)));
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[jj][s2], o[dt], 0, 0, 0);
+        }
       }
-    }
   };
 
   __syncthreads();
@@ -245,9 +299,9 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     }
     __syncthreads();
     // prologue: K(0), V(0), K(1) resident, then S(0)
-    issue(0, k0, false);
-    issue(0, v0, true);
-    if (nt > 1) issue(1, k1, false);
+    issue(0, B0());
+    issue(0, B2());
+    if (nt > 1) issue(1, B1());
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     qk(sa, k0);
@@ -255,66 +309,81 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     // reading K(0) first
     if (nt > 2) __syncthreads();
     for (int i = 0; i < nt; i += 2) {
-      if (i + 2 < nt) issue(i + 2, k0, false);
-      if (i + 1 < nt) issue(i + 1, v1, true);
+      if (i + 2 < nt) issue(i + 2, B0());
+      if (i + 1 < nt) issue(i + 1, B3());
       interval(i, sa, sb, k1, v0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (i + 1 >= nt) break;
-      if (i + 3 < nt) issue(i + 3, k1, false);
-      if (i + 2 < nt) issue(i + 2, v0, true);
+      if (i + 3 < nt) issue(i + 3, B1());
+      if (i + 2 < nt) issue(i + 2, B2());
       interval(i + 1, sb, sa, k0, v1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
 
-  // merge the two key halves of every query group, normalise, store
+  // with key halves, merge the two halves of every (head, query group) pair
+  // through LDS; normalise, store
   const float l_w = halves_sum(l_run);
-  uint8_t *const mbuf = qg == 0 ? (uint8_t *)k0 : qg == 1 ? (uint8_t *)v0 : qg == 2 ? (uint8_t *)k1 : (uint8_t *)v1;
-  float *scratch = reinterpret_cast<float *>(mbuf);
-  if (kh == 1) {
+  float m = m_run, l_tot = l_w, a1 = 1.f, a2 = 0.f;
+  const float *scratch = nullptr;
+  if constexpr (KSPLIT == 2) {
+    uint8_t *const mbuf = gi == 0 ? k0 : gi == 1 ? v0 : gi == 2 ? k1 : v1;
+    float *sc = reinterpret_cast<float *>(mbuf);
+    scratch = sc;
+    if (kh == 1) {
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<f32x4 *>(scratch + ((dt * 4 + i4) * 64 + lane) * 4) =
-            f32x4{o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
-    mrg_ml[qg][0][lane] = m_run;
-    mrg_ml[qg][1][lane] = l_w;
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4 *>(sc + ((dt * 4 + i4) * 64 + lane) * 4) =
+              f32x4{o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
+      mrg_ml[gi][0][lane] = m_run;
+      mrg_ml[gi][1][lane] = l_w;
+    }
+    __syncthreads();
+    if (kh != 0) return;
+    const float m2 = mrg_ml[gi][0][lane];
+    const float l2 = mrg_ml[gi][1][lane];
+    m = fmaxf(m_run, m2);
+    a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
+    l_tot = l_w * a1 + l2 * a2;
   }
-  __syncthreads();
-  if (kh != 0 || !qok) return;
-  const float m2 = mrg_ml[qg][0][lane];
-  const float l2 = mrg_ml[qg][1][lane];
-  const float m = fmaxf(m_run, m2);
-  const float a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-  const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
-  const float l_tot = l_w * a1 + l2 * a2;
+  if (!qok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   uint16_t *ob16 = p.o + b * p.os0 + h * p.os1 + (int64_t)qi * p.os2;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 o2 = *reinterpret_cast<const f32x4 *>(scratch + ((dt * 4 + i4) * 64 + lane) * 4);
-      const float x0 = (o[dt][4 * i4] * a1 + o2[0] * a2) * inv;
-      const float x1 = (o[dt][4 * i4 + 1] * a1 + o2[1] * a2) * inv;
-      const float x2 = (o[dt][4 * i4 + 2] * a1 + o2[2] * a2) * inv;
-      const float x3 = (o[dt][4 * i4 + 3] * a1 + o2[3] * a2) * inv;
+      f32x4 x = {o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
+      if constexpr (KSPLIT == 2) {
+        const f32x4 o2 = *reinterpret_cast<const f32x4 *>(scratch + ((dt * 4 + i4) * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = x[e] * a1 + o2[e] * a2;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= inv;
       *reinterpret_cast<uint2 *>(ob16 + 32 * dt + 8 * i4 + 4 * hf) =
-          make_uint2(cvt_pk_bf16(x0, x1), cvt_pk_bf16(x2, x3));
+          make_uint2(cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3]));
     }
-  if (p.lse && hf == 0) p.lse[bh * N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (p.lse && hf == 0) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-#define BSA_TOK_KERNEL(BQ)                                                                          \
-  __global__ __attribute__((amdgpu_flat_work_group_size(4 * BQ, 4 * BQ), amdgpu_waves_per_eu(2, 2)))   \
-  void attn_tok_##BQ(const TokParams p) {                                                          \
-    attn_tok_body<BQ>(p);                                                                          \
+// 64-query sets: 4 wavefronts (two query groups x key halves), two per CU;
+// 128-query sets and pairs of 64-query sets: 4 wavefronts that each take
+// whole tiles, two per CU
+#define BSA_TOK_KERNEL(NAME, BQ, HP, KSPLIT)                                                        \
+  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))      \
+  void NAME(const TokParams p) {                                                                   \
+    static_assert(TCfg<BQ, HP, KSPLIT>::NT == 256, "four wavefronts");                             \
+    attn_tok_body<BQ, HP, KSPLIT>(p);                                                               \
   }
-BSA_TOK_KERNEL(64)
-BSA_TOK_KERNEL(128)
+BSA_TOK_KERNEL(attn_tok_64, 64, 1, 2)
+BSA_TOK_KERNEL(attn_tok_128, 128, 1, 1)
+BSA_TOK_KERNEL(attn_tok_64x2, 64, 2, 1)
 #undef BSA_TOK_KERNEL
 
 bool bad_strides(const int64_t s[3]) {
@@ -333,6 +402,8 @@ extern "C" int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream) {
   if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->N <= 0 || a->n_sets < 0) return BSA_ERR_ARG;
   if (a->Hq % a->Hkv) return BSA_ERR_ARG;
   if (a->d != 128 || (a->set_size != 64 && a->set_size != 128)) return BSA_ERR_UNSUPPORTED;
+  if (a->kv_share != 0 && a->kv_share != 2) return BSA_ERR_ARG;
+  if (a->kv_share == 2 && (a->set_size != 64 || (a->Hq / a->Hkv) % 2)) return BSA_ERR_UNSUPPORTED;
   if (!bsa_aligned16(a->q) || !bsa_aligned16(a->k) || !bsa_aligned16(a->v) || !bsa_aligned16(a->o))
     return BSA_ERR_ARG;
   if (tok::bad_strides(a->q_str) || tok::bad_strides(a->k_str) || tok::bad_strides(a->v_str) ||
@@ -370,8 +441,9 @@ extern "C" int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream) {
   const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->d);
   p.c = scale * kLog2e;
   hipStream_t s = bsa_hip_stream(stream);
-  if (a->set_size == 64) hipLaunchKernelGGL(tok::attn_tok_64, dim3((unsigned)n_sets), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(tok::attn_tok_128, dim3((unsigned)n_sets), dim3(512), 0, s, p);
+  if (a->kv_share == 2) hipLaunchKernelGGL(tok::attn_tok_64x2, dim3((unsigned)(n_sets / 2)), dim3(256), 0, s, p);
+  else if (a->set_size == 64) hipLaunchKernelGGL(tok::attn_tok_64, dim3((unsigned)n_sets), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(tok::attn_tok_128, dim3((unsigned)n_sets), dim3(256), 0, s, p);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

@@ -183,6 +183,9 @@ def _tok_args(**kw):
     (dict(o=FAKE), _lib.BSA_ERR_ARG),
     (dict(N=1 << 23), _lib.BSA_ERR_UNSUPPORTED),
     (dict(kv_idx=None), _lib.BSA_ERR_ARG),
+    (dict(kv_share=1), _lib.BSA_ERR_ARG),
+    (dict(kv_share=2, set_size=128), _lib.BSA_ERR_UNSUPPORTED),
+    (dict(kv_share=2, Hkv=4), _lib.BSA_ERR_UNSUPPORTED),                                   # G = 1: no pairs
 ])
 def test_attn_tok_argument_errors(L, kw, code):
     a = _tok_args(**kw)

@@ -47,7 +47,12 @@ def test_config_parity(name):
         assert np.array_equal(res.perm_q.cpu().numpy(), pq)
         assert np.array_equal(res.perm_k.cpu().numpy(), pk)
     W = 2048   # wave_rows = 0 selects one bucket per segment of up to 2048 rows
-    assert np.array_equal(res.order.cpu().numpy(), oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8))
+    # the prefill pattern is the same for every head: the pipeline serves
+    # query-head pairs in one launch, from a head-step-2 schedule
+    assert res.kv_share == (name == "llm_prefill")
+    hs = 2 if res.kv_share else 1
+    assert np.array_equal(res.order.cpu().numpy(),
+                          oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8, head_step=hs))
     _log("  integer steps bit-exact (nnz=%d)" % rp[-1])
     # stage-1 order of every head and the schedule built on it
     gp, ga = api.spectral_order(res.row_ptr, res.col, w.B * w.Hq, w.nQB, w.nQB, 10, want_angle=True)

@@ -3,10 +3,13 @@ sections 3 and 4.8; MC-Sparse token-level KV selection), called through the
 C ABI, against the oracle on the same seeded inputs.
 
 Cases: random sets with lists of every awkward length (empty, 1, 63, 64,
-65, over a 1024-entry staging chunk), out-of-range and duplicate entries,
-empty query slots, GQA, full and causal masking, 64- and 128-query sets;
-INTRA's Scatter, Gather 1 and Gather 0 maps; a token-selection workload of MC-Sparse's
-shape.  Bar: max-abs 2e-2, mean-abs 2e-3 on O, 1e-3 on LSE; rows that no set
+65, over a 1024- and a 2048-entry staging chunk), out-of-range and duplicate
+entries, empty query slots, GQA, full and causal masking, 64- and 128-query
+sets; INTRA's Scatter, Gather 1 and Gather 0 maps; a token-selection workload
+of MC-Sparse's shape.  The head-pair launch (kv_share: the sets of query
+heads 2j and 2j + 1 of a KV group are identical, each gathered tile serves
+both) is checked against the oracle and, within the same bar, against the
+per-head launch.  Bar: max-abs 2e-2, mean-abs 2e-3 on O, 1e-3 on LSE; rows that no set
 lists stay untouched.
 """
 import numpy as np
@@ -16,7 +19,7 @@ import torch
 import oracle
 from block_sparse_attention_mask_amd import api
 import synth
-from parity_common import assert_within
+from parity_common import LSE_ABS, MAX_ABS, assert_within
 
 pytestmark = pytest.mark.gpu
 
@@ -35,12 +38,27 @@ def _qkv(seed, B, Hq, Hkv, N, d=128, scale_q=1.0):
     return f(Hq, scale_q), f(Hkv, 1.0), f(Hkv, 1.0)
 
 
-def _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, label, slots=None):
+def _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, label, slots=None, kv_share=False):
     B, Hq, N, d = q.shape
     C, BQ = q_idx.shape[1], q_idx.shape[2]
-    out, lse = api.attn_tok_fwd(_gpu(q.view(np.int16)), _gpu(k.view(np.int16)), _gpu(v.view(np.int16)),
-                                _gpu(q_idx), _gpu(kv_ptr), _gpu(kv_idx), want_lse=True, causal=causal)
+    args = (_gpu(q.view(np.int16)), _gpu(k.view(np.int16)), _gpu(v.view(np.int16)), _gpu(q_idx), _gpu(kv_ptr),
+            _gpu(kv_idx))
+    out, lse = api.attn_tok_fwd(*args, want_lse=True, causal=causal, kv_share=kv_share)
     torch.cuda.synchronize()
+    if kv_share:
+        # the per-head launch splits every tile's keys over two wavefronts and
+        # merges them at the end; the pair launch walks whole tiles: same
+        # values up to rounding order
+        ref_out, ref_lse = api.attn_tok_fwd(*args, want_lse=True, causal=causal)
+        torch.cuda.synchronize()
+        a_ = synth.bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
+        b_ = synth.bf16_bits_to_f32(ref_out.cpu().numpy().view(np.uint16))
+        assert np.abs(a_ - b_).max() <= MAX_ABS
+        la, lb = lse.cpu().numpy(), ref_lse.cpu().numpy()
+        assert np.array_equal(np.isnan(la), np.isnan(lb))
+        fin = np.isfinite(la) & np.isfinite(lb)
+        assert np.array_equal(np.isneginf(la), np.isneginf(lb))
+        assert np.abs(la[fin] - lb[fin]).max(initial=0.0) <= LSE_ABS
     go = synth.bf16_bits_to_f32(out.cpu().numpy().view(np.uint16)).reshape(B * Hq, N, d)
     gl = lse.cpu().numpy()
     if slots is None:
@@ -112,6 +130,47 @@ def test_intra_gather1(causal):
     maps = synth.cqs_per_head(synth.cqs_gather1(N, 8, 64, causal), B * Hq)
     _log("case tok INTRA Gather 1 N=%d causal=%d" % (N, causal))
     _run_and_compare(q, k, v, *maps, causal, "gather1")
+
+
+def _pair_identical_sets(g, B, Hq, N, C, BQ, lens):
+    """Random sets drawn per even head and copied to its partner head."""
+    q_idx = np.full((B * Hq, C, BQ), -1, np.int32)
+    lists = [None] * (B * Hq * C)
+    for h in range(0, B * Hq, 2):
+        pos = g.permutation(N)[:C * BQ - 5]
+        flat = np.full(C * BQ, -1, np.int32)
+        flat[g.permutation(C * BQ)[:len(pos)]] = pos
+        q_idx[h] = q_idx[h + 1] = flat.reshape(C, BQ)
+        for c in range(C):
+            keys = g.integers(0, N, size=lens[c]).astype(np.int32)
+            if lens[c] > 10:
+                keys[3] = -1
+                keys[4] = N + 7
+                keys[5] = keys[6]
+            lists[h * C + c] = lists[(h + 1) * C + c] = keys
+    kv_ptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    return q_idx, kv_ptr, np.concatenate(lists).astype(np.int32)
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv", [(False, 2, 1), (True, 4, 2), (False, 8, 2)])
+def test_head_pairs_random_sets(causal, Hq, Hkv):
+    B, N, C, BQ = 1, 5000, 10, 64
+    q, k, v = _qkv(60 + causal + Hq, B, Hq, Hkv, N)
+    g = np.random.default_rng(61 + Hq)
+    lens = np.array([0, 1, 63, 64, 65, 300, 2100, 7, 129, 2048])
+    q_idx, kv_ptr, kv_idx = _pair_identical_sets(g, B, Hq, N, C, BQ, lens)
+    _log("case tok head pairs random causal=%d Hq=%d Hkv=%d" % (causal, Hq, Hkv))
+    _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, "head pairs", kv_share=True)
+
+
+@pytest.mark.parametrize("pattern", ["scatter", "gather1"])
+def test_head_pairs_intra(pattern):
+    B, Hq, Hkv, N = 1, 8, 2, 4096 + 40
+    q, k, v = _qkv(70 + len(pattern), B, Hq, Hkv, N)
+    f = synth.cqs_scatter if pattern == "scatter" else synth.cqs_gather1
+    maps = synth.cqs_per_head(f(N, 8, 64, True), B * Hq)
+    _log("case tok head pairs INTRA %s N=%d" % (pattern, N))
+    _run_and_compare(q, k, v, *maps, True, pattern + " head pairs", kv_share=True)
 
 
 def test_intra_gather0():
