@@ -380,7 +380,11 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     auto m_phase = [&](int j, auto par) -> Pre {
       constexpr int P = decltype(par)::value;   // j & 1
       const Pre pr = pre_of(j);
+      // the matrix step issues ahead of the softmax step of the SIMD's other
+      // wavefront: its MFMAs and operand reads are not held up behind VALU work
+      __builtin_amdgcn_s_setprio(1);
       mstep(smem + (P ? VM0 : VM1) * C::KB, smem + (P ? KM1 : KM0) * C::KB);
+      __builtin_amdgcn_s_setprio(0);
       pin_results();
       end_phase();
       return pr;

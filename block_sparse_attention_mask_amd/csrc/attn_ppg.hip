@@ -306,7 +306,11 @@ __device__ __forceinline__ void attn_ppg_body(const AttnParams &p, const int32_t
     auto m_phase = [&](int j, auto kc) -> Pre {
       constexpr int K3 = decltype(kc)::value;   // j % 3
       const Pre pr = pre_of(j);
+      // the matrix step issues ahead of the softmax step of the SIMD's other
+      // wavefront: its MFMAs and operand reads are not held up behind VALU work
+      __builtin_amdgcn_s_setprio(1);
       mstep(smem + (3 + (K3 + 2) % 3) * C::KB, smem + K3 * C::KB);
+      __builtin_amdgcn_s_setprio(0);
       pin_results();
       end_phase();
       return pr;
