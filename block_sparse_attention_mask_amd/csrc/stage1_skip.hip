@@ -4,19 +4,23 @@
 // on the device from the CSR lists, so a pass that uses it makes no host
 // round trip: the decision is a device flag that the stage-1 kernel reads.
 //
-// Statistics (integers, exact): nnz = listed blocks (entries in [0, nKB)),
-// nmax = the largest per-head nnz, fresh = entries of each row that the
-// previous row of the same head does not list (rows ascending, as the
-// attention kernels require; a two-pointer merge per row).  Then, in fp64:
-// f = fresh / nnz, density = nnz / (BH nQB nKB), t_attn = nnz * tile_ms *
-// (block/128)^2 * (d/128) / n_cus, gain = gamma f t_attn, cost = (iters/10)
-// (row_ms nQB + nnz_ms nmax), K/V bytes of a head = 4 N d.  Stage 1 runs when
-// the K/V of a head exceed l2_bytes, density >= density_min, gain > cost and
-// the stage-1 kernel supports the shape.
+// Statistics (integers, exact): nnz = listed entries (every entry is one
+// tile the attention kernel processes), nmax = the largest per-head nnz,
+// fresh = entries of each row whose block the previous row of the same head
+// does not list (rows ascending, as the list builder writes them).  Then, in
+// fp64: f = fresh / nnz, density = nnz / (BH nQB nKB), t_attn = nnz * tile_ms
+// * (block/128)^2 * (d/128) / n_cus, gain = gamma f t_attn, cost = (iters/10)
+// (row_ms nQB + nnz_ms nmax), K/V bytes of a head = 4 N d.  Stage 1 runs
+// when the K/V of a head exceed l2_bytes, density >= density_min, gain > cost
+// and the stage-1 kernel supports the shape.
 //
-// One workgroup walks every head (its threads over the head's rows) and
-// reduces in a fixed order, so the statistics and the decision do not depend
-// on timing.
+// Three launches: the decision word is cleared; one wavefront per row looks
+// every entry up in the previous row (binary search over the ascending list)
+// and adds its fresh count to the decision word with an integer atomic; one
+// workgroup reads nnz and nmax off the row offsets, forms the estimate and
+// overwrites the word with the decision.  Integer sums do not depend on the
+// order of the atomics, so the statistics and the decision do not depend on
+// timing.
 #include "bsa_internal.h"
 
 // the decision's expressions are evaluated unfused, like the reference
@@ -25,53 +29,60 @@
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;   // one wavefront per row
 
-__device__ int64_t block_sum_i64(int64_t x, int64_t *red) {
-  const int t = threadIdx.x;
-  red[t] = x;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  const int64_t r = red[0];
-  __syncthreads();
-  return r;
+__global__ void clear_kernel(int32_t *__restrict__ word) {
+  if (threadIdx.x == 0) word[0] = 0;
 }
 
-__global__ __launch_bounds__(kThreads) void stage1_decide_kernel(const int32_t *__restrict__ row_ptr,
-                                                                 const int32_t *__restrict__ col, int BH, int nQB,
-                                                                 int nKB, int64_t N, int d, int block, int iters,
-                                                                 int n_cus, bsa_stage1_params prm,
+__global__ __launch_bounds__(kThreads) void fresh_kernel(const int32_t *__restrict__ row_ptr,
+                                                         const int32_t *__restrict__ col, int nQB, int64_t R,
+                                                         int32_t *__restrict__ fresh) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int u = (int)(r % nQB);
+  const int32_t a0 = row_ptr[r], a1 = row_ptr[r + 1];
+  const int32_t b0 = u > 0 ? row_ptr[r - 1] : a0, b1 = a0;   // the previous row (empty for u = 0)
+  int32_t cnt = 0;
+  for (int32_t e = a0 + lane; e < a1; e += 64) {
+    const int32_t v = col[e];
+    // first position in [b0, b1) holding a block >= v
+    int32_t lo = b0, hi = b1;
+    while (lo < hi) {
+      const int32_t mid = lo + (hi - lo) / 2;
+      if (col[mid] < v) lo = mid + 1;
+      else hi = mid;
+    }
+    if (!(lo < b1 && col[lo] == v)) ++cnt;
+  }
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if (lane == 0 && cnt) atomicAdd(fresh, cnt);
+}
+
+__global__ __launch_bounds__(kThreads) void stage1_decide_kernel(const int32_t *__restrict__ row_ptr, int BH,
+                                                                 int nQB, int nKB, int64_t N, int d, int block,
+                                                                 int iters, int n_cus, bsa_stage1_params prm,
                                                                  int32_t *__restrict__ decision,
                                                                  double *__restrict__ stats) {
   __shared__ int64_t red[kThreads];
   const int t = threadIdx.x;
-  int64_t nnz = 0, nmax = 0, fresh = 0;
-  for (int h = 0; h < BH; ++h) {
-    int64_t my_n = 0, my_f = 0;
-    for (int u = t; u < nQB; u += kThreads) {
-      const int64_t r = (int64_t)h * nQB + u;
-      const int32_t a0 = row_ptr[r], a1 = row_ptr[r + 1];
-      int32_t b = u > 0 ? row_ptr[r - 1] : a0;
-      const int32_t b1 = a0;   // the previous row is [row_ptr[r - 1], a0), empty for u = 0
-      for (int32_t e = a0; e < a1; ++e) {
-        const int32_t v = col[e];
-        if (v < 0 || v >= nKB) continue;
-        ++my_n;
-        // advance the previous row's pointer to the first entry >= v
-        while (b < b1 && col[b] < v) ++b;
-        if (!(b < b1 && col[b] == v)) ++my_f;
-      }
-    }
-    const int64_t nh = block_sum_i64(my_n, red);
-    const int64_t fh = block_sum_i64(my_f, red);
-    nnz += nh;
-    fresh += fh;
-    if (nh > nmax) nmax = nh;
+  int64_t my_max = 0;
+  for (int h = t; h < BH; h += kThreads) {
+    const int64_t nh = (int64_t)row_ptr[(int64_t)(h + 1) * nQB] - row_ptr[(int64_t)h * nQB];
+    if (nh > my_max) my_max = nh;
+  }
+  red[t] = my_max;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (t < s && red[t + s] > red[t]) red[t] = red[t + s];
+    __syncthreads();
   }
   if (t != 0) return;
+  const int64_t nmax = red[0];
+  const int64_t nnz = (int64_t)row_ptr[(int64_t)BH * nQB] - row_ptr[0];
+  const int64_t fresh = decision[0];
   const double f = nnz > 0 ? (double)fresh / (double)nnz : 0.0;
   const double density = (double)nnz / ((double)BH * (double)nQB * (double)nKB);
   const double bs = (double)block / 128.0;
@@ -117,8 +128,15 @@ extern "C" int bsa_stage1_decide(const int32_t *row_ptr, const int32_t *col, int
   bsa_stage1_params prm;
   if (params) prm = *params;
   else bsa_stage1_default_params(&prm);
-  hipLaunchKernelGGL(stage1_decide_kernel, dim3(1), dim3(kThreads), 0, bsa_hip_stream(stream), row_ptr, col, BH,
-                     nQB, nKB, N, d, block, iters, n_cus, prm, decision, stats);
+  hipStream_t s = bsa_hip_stream(stream);
+  const int64_t R = (int64_t)BH * nQB;
+  hipLaunchKernelGGL(clear_kernel, dim3(1), dim3(64), 0, s, decision);
+  BSA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(fresh_kernel, dim3((unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(kThreads), 0, s,
+                     row_ptr, col, nQB, R, decision);
+  BSA_LAUNCH_CHECK();
+  hipLaunchKernelGGL(stage1_decide_kernel, dim3(1), dim3(kThreads), 0, s, row_ptr, BH, nQB, nKB, N, d, block, iters,
+                     n_cus, prm, decision, stats);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

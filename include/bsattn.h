@@ -220,10 +220,11 @@ int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, i
  * device so that no host round trip is needed.
  *
  * Over the BH heads' CSR rows (row_ptr device int32 [BH*nQB + 1], col device
- * int32, every row ascending; entries outside [0, nKB) are not counted):
- * nnz = listed blocks, nmax = the largest per-head nnz, fresh = entries a
- * row lists that the previous row of its head does not (all of the first
- * row's).  With f = fresh/nnz, density = nnz/(BH nQB nKB),
+ * int32, every row ascending as bsa_csr_fill writes them; for other lists
+ * fresh is unspecified): nnz = listed entries (each is one tile the
+ * attention kernels process), nmax = the largest per-head nnz, fresh =
+ * entries a row lists whose block the previous row of its head does not
+ * list (all of the first row's).  With f = fresh/nnz, density = nnz/(BH nQB nKB),
  * t_attn = nnz tile_ms (block/128)^2 (d/128) / n_cus (ms), gain = gamma f
  * t_attn, cost = (iters/10)(row_ms nQB + nnz_ms nmax) (ms): stage 1 runs when
  * 4 N d (bytes of K and V of a head) > l2_bytes, density >= density_min,
@@ -234,8 +235,10 @@ int bsa_spectral_order(const int32_t *row_ptr, const int32_t *col, int32_t BH, i
  * (output, 0 or 1).  stats: device float64 [7] (output, may be NULL): f,
  * density, t_attn, gain, cost, K/V bytes per head, decision.
  * BSA_ERR_ARG for NULL pointers or non-positive sizes / iters / n_cus;
- * BSA_ERR_UNSUPPORTED for BH*nQB >= 2^31.  Asynchronous (one workgroup
- * walks all heads; its reductions run in a fixed order).
+ * BSA_ERR_UNSUPPORTED for BH*nQB >= 2^31.  Asynchronous (three launches: the
+ * fresh count is an integer sum over one wavefront per row, so the
+ * statistics do not depend on timing; decision[0] holds that count until
+ * the last launch overwrites it with the decision).
  * ------------------------------------------------------------------------- */
 typedef struct {
   double gamma, tile_ms, row_ms, nnz_ms, density_min, l2_bytes;

@@ -430,10 +430,11 @@ int oracle_spectral_order(const int32_t *row_ptr, const int32_t *col, int64_t BH
  * does not exceed its overhead; reordering was skipped at low retained
  * densities (1.7 %, 6.7 %) and enabled from 14.5 %.  The pages give the
  * estimate in words only; this is the reading, step by step:
- *   nnz   = listed blocks (entries in [0, nKB)) over all BH heads;
+ *   nnz   = listed entries over all BH heads (each entry is one tile the
+ *           attention kernel processes, whatever block it names);
  *   nmax  = the largest per-head nnz (heads are reordered in parallel);
- *   fresh = sum over rows of the blocks the row lists and the row before it
- *           in the same head does not (the first row of a head: all), so
+ *   fresh = sum over rows of the entries whose block the row before it in
+ *           the same head does not list (the first row of a head: all), so
  *           f = fresh / nnz is the share of K/V block visits that the
  *           current order does not pair with the previous row;
  *   density = nnz / (BH nQB nKB);
@@ -461,7 +462,6 @@ int oracle_stage1_decide(const int32_t *row_ptr, const int32_t *col, int64_t BH,
       const int64_t r = h * nQB + u;
       for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
         const int32_t v = col[e];
-        if (v < 0 || v >= nKB) continue;
         ++nh;
         int in_prev = 0;
         if (u > 0)

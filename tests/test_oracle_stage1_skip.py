@@ -54,14 +54,18 @@ def test_fresh_fraction_and_density_match_brute_force(seed):
     assert st["density"] == pytest.approx(rp[-1] / (BH * nQB * nKB), abs=1e-15)
 
 
-def test_entries_outside_the_blocks_are_not_counted():
+def test_every_listed_entry_counts():
+    """An entry naming a block outside [0, nKB) is still a tile the attention
+    kernels process: it counts in nnz, and it is fresh unless the previous row
+    lists the same block."""
     rp, col = csr_from_lists([[0, 1], [1, 2]])
     col_bad = col.copy()
     col_bad[0] = 99
     _, a = oracle.stage1_decide(rp, col, 1, 2, 3, 256, 128, 128, 10, 256)
     _, b = oracle.stage1_decide(rp, col_bad, 1, 2, 3, 256, 128, 128, 10, 256)
-    assert a["density"] == pytest.approx(4 / 6) and b["density"] == pytest.approx(3 / 6)
-    assert b["fresh_fraction"] == pytest.approx(2 / 3)
+    assert a["density"] == pytest.approx(4 / 6) and b["density"] == pytest.approx(4 / 6)
+    assert a["fresh_fraction"] == pytest.approx(3 / 4)    # 0, 1 of row 0; 2 of row 1
+    assert b["fresh_fraction"] == pytest.approx(3 / 4)    # 99, 1 of row 0; 2 of row 1
 
 
 def big_case(shared, density=0.3, nQB=512, BH=64, seed=5):
