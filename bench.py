@@ -80,7 +80,7 @@ def dense_launches(torch, n):
     vt = api.transpose_rows(v)
     nb = N // 128
     rp, col, _ = api.build_csr(torch.ones(H * nb, nb, dtype=torch.uint8, device="cuda"), nQB=nb)
-    order = api.schedule(rp, 1, H, H, nb, 2048, 8)
+    order = api.schedule(rp, 1, H, H, nb, 0, 8, col=col)
     out = torch.empty_like(q)
     s = torch.cuda.current_stream()
     ms = []
@@ -317,7 +317,7 @@ def attention_alone(dw, args, torch, crm=False):
     v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
     share = kv_share_ok(dw, row_ptr, col, lw) and not crm
     order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
-                         head_step=2 if share else 1)
+                         head_step=2 if share else 1, col=col)
     out = torch.empty((dw.B, dw.Hq, dw.N, dw.d), dtype=q.dtype, device=q.device)
 
     def launch():   # the query gather and the output scatter are fused into the kernel
@@ -401,7 +401,7 @@ def sampler_stage(dw, torch, m_exact=8, m_sample=8):
             for i, n in enumerate(names):
                 times[n].append(ev[i].elapsed_time(ev[i + 1]))
     row_ptr, col, lw = res
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, 0, 8)
+    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, 0, 8, col=col)
     ms = []
     for it in range(12):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -722,7 +722,7 @@ def stage_times(pipeline, dw, args, torch):
     share = kv_share_ok(dw, row_ptr, col, lw)
     ev[3].record(s)
     order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm,
-                         head_step=2 if share else 1)
+                         head_step=2 if share else 1, col=col)
     ev[4].record(s)
     api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
                  gather_perm_q=pq, causal=dw.causal, v_dim_major=True, kv_share=share)

@@ -128,7 +128,7 @@ def load():
         L.bsa_transpose_rows.restype = ctypes.c_int
         L.bsa_transpose_rows.argtypes = [P, P, P, I32, I32, I64, I32, I64, P, P, P]
         L.bsa_schedule.restype = ctypes.c_int
-        L.bsa_schedule.argtypes = [P, I32, I32, I32, I32, I32, I32, P, I32, P, P]
+        L.bsa_schedule.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, I32, P, P]
         L.bsa_pair_rows_equal.restype = ctypes.c_int
         L.bsa_pair_rows_equal.argtypes = [P, P, P, I32, I32, I32, I32, P, P]
         L.bsa_spectral_order.restype = ctypes.c_int

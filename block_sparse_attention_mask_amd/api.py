@@ -302,17 +302,22 @@ def transpose_rows(src: torch.Tensor, perm: Optional[torch.Tensor] = None, ld: O
 
 def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_rows: int = 0,
              n_xcd: int = 8, order=None, stream=None, row_perm: Optional[torch.Tensor] = None,
-             head_step: int = 1) -> torch.Tensor:
+             head_step: int = 1, col: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Launch order of the attention rows; head_step 2 lists one row per pair
-    of query heads sharing a KV head (for attn_fwd(kv_share=True))."""
+    of query heads sharing a KV head (for attn_fwd(kv_share=True)).  With
+    wave_rows 0 and the block lists ``col``, each segment keeps the sorted or
+    the sequence order, whichever shares more blocks between consecutive
+    rows."""
     _dev(row_ptr, "row_ptr", torch.int32)
+    if col is not None:
+        _dev(col, "col", torch.int32)
     if row_perm is not None:
         _dev(row_perm, "row_perm", torch.int32)
         if row_perm.numel() != B * Hq * nQB:
             raise ValueError("row_perm must hold B*Hq*nQB entries")
     if order is None:
         order = torch.empty(B * Hq * nQB // head_step, dtype=torch.int32, device=row_ptr.device)
-    check("bsa_schedule", load().bsa_schedule(_ptr(row_ptr), B, Hq, Hkv, nQB, int(wave_rows), int(n_xcd),
+    check("bsa_schedule", load().bsa_schedule(_ptr(row_ptr), _ptr(col), B, Hq, Hkv, nQB, int(wave_rows), int(n_xcd),
                                               _ptr(row_perm), int(head_step), _ptr(order), _stream(stream)))
     return order
 

@@ -24,6 +24,14 @@
 // One workgroup per bucket: keys (INT32_MAX - nnz) << 32 | position are
 // sorted ascending with a bitonic network in LDS.
 //
+// With whole-segment buckets and the block lists given, a bucket keeps the
+// sorted order only if consecutive rows share at least as many blocks as in
+// the sequence order (the rows an XCD runs one after another reuse each
+// other's K/V in its L2): sorting by length groups the rows of one cluster of
+// a permuted head, but scatters the neighbouring rows of a banded or local
+// pattern.  Shared blocks are estimated with a 256-bit signature per row (bit
+// v mod 256 of each listed block v), kept in LDS.
+//
 // bsa_pair_rows_equal checks the precondition of that pair kernel: one
 // wavefront per pair of rows compares lengths, block indices and log-weight
 // bits, and clears a flag on any difference.
@@ -33,11 +41,21 @@ namespace {
 
 constexpr int kMaxWave = 2048;
 
-__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ row_ptr, int Hq,
-                                                        int Hkv, int nQB, int W, int n_xcd,
-                                                        int64_t R, const int32_t *__restrict__ row_perm,
-                                                        int hs, int32_t *__restrict__ order) {
+__device__ __forceinline__ int sig_fresh(const uint64_t *a, const uint64_t *prev) {
+  int c = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) c += __popcll(a[w] & ~(prev ? prev[w] : 0ull));
+  return c;
+}
+
+__global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restrict__ row_ptr,
+                                                        const int32_t *__restrict__ col, int Hq, int Hkv,
+                                                        int nQB, int W, int n_xcd, int64_t R,
+                                                        const int32_t *__restrict__ row_perm, int hs,
+                                                        int32_t *__restrict__ order) {
   __shared__ uint64_t key[kMaxWave];
+  __shared__ uint64_t sig[kMaxWave][4];   // block signatures (adaptive mode)
+  __shared__ int cost[2];                 // sorted, sequence
   const int G = Hq / Hkv, Gs = G / hs;   // scheduled heads per KV head: every hs-th
   const int64_t seg = (int64_t)Gs * nQB;
   const int64_t nbk = (seg + W - 1) / W;           // buckets per (b, g) segment
@@ -60,9 +78,20 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       const int64_t r = row_at(k * W + i);          // position within the segment
       const int32_t nnz = r >= 0 ? row_ptr[r + 1] - row_ptr[r] : 0;
       kk = ((uint64_t)(uint32_t)(0x7fffffff - nnz) << 32) | (uint32_t)i;
+      if (col) {
+        uint64_t sg[4] = {0, 0, 0, 0};
+        if (r >= 0)
+          for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+            const uint32_t bit = (uint32_t)col[e] & 255u;
+            sg[bit >> 6] |= 1ull << (bit & 63);
+          }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sig[i][w] = sg[w];
+      }
     }
     key[i] = kk;
   }
+  if (threadIdx.x < 2) cost[threadIdx.x] = 0;
   __syncthreads();
   for (int size = 2; size <= P2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -79,8 +108,21 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       __syncthreads();
     }
   }
+  bool keep_seq = false;
+  if (col) {
+    int cs = 0, cq = 0;
+    for (int i = threadIdx.x; i < n; i += 1024) {
+      const int a = (int)(key[i] & 0xffffffffu), p = i ? (int)(key[i - 1] & 0xffffffffu) : 0;
+      cs += sig_fresh(sig[a], i ? sig[p] : nullptr);
+      cq += sig_fresh(sig[i], i ? sig[i - 1] : nullptr);
+    }
+    atomicAdd(&cost[0], cs);
+    atomicAdd(&cost[1], cq);
+    __syncthreads();
+    keep_seq = cost[1] < cost[0];
+  }
   for (int i = threadIdx.x; i < n; i += 1024) {
-    const int src = (int)(key[i] & 0xffffffffu);
+    const int src = keep_seq ? i : (int)(key[i] & 0xffffffffu);
     const int32_t r = (int32_t)row_at(k * W + src);
     const int64_t P = start + i;                    // logical position
     int64_t launch = P;
@@ -136,9 +178,9 @@ extern "C" int bsa_pair_rows_equal(const int32_t *row_ptr, const int32_t *col, c
   return BSA_OK;
 }
 
-extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
-                            int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm, int32_t head_step,
-                            int32_t *order, bsa_stream_t stream) {
+extern "C" int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t nQB, int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm,
+                            int32_t head_step, int32_t *order, bsa_stream_t stream) {
   if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
   if (Hq % Hkv) return BSA_ERR_ARG;
   if (head_step != 1 && head_step != 2) return BSA_ERR_ARG;
@@ -153,8 +195,9 @@ extern "C" int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32
   const int W = wave_rows ? wave_rows : kMaxWave;
   const int64_t seg = (int64_t)(Hq / Hkv / head_step) * nQB;
   const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
+  // the order choice applies to whole-segment buckets (wave_rows = 0)
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),
-                     row_ptr, Hq, Hkv, nQB, W, n_xcd, R, row_perm, head_step, order);
+                     row_ptr, wave_rows ? nullptr : col, Hq, Hkv, nQB, W, n_xcd, R, row_perm, head_step, order);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

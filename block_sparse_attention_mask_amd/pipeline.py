@@ -195,7 +195,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     share = False if crm else _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, stream)
     if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
-                             row_perm=row_perm, head_step=2 if share else 1)
+                             row_perm=row_perm, head_step=2 if share else 1, col=col)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
@@ -238,7 +238,7 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
     if schedule:
         row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
-                             row_perm=row_perm)
+                             row_perm=row_perm, col=col)
     sperm = perm_q if fuse_scatter else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
@@ -292,7 +292,7 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
     share = _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, main)
     if schedule:
         order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main,
-                             row_perm=row_perm, head_step=2 if share else 1)
+                             row_perm=row_perm, head_step=2 if share else 1, col=col)
     main.wait_stream(side)
     for t in (perm_k, k, v):
         if t is not None:

@@ -344,7 +344,15 @@ int bsa_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_ptr
  * the list is dealt to launch indices so that the GPU's round-robin dispatch
  * gives XCD x the x-th contiguous slice:
  * order[i] = logical[start(i % n_xcd) + i / n_xcd].  wave_rows = 0 selects
- * 2048 (a whole segment of up to 2048 rows is one bucket).  head_step 1
+ * 2048 (a whole segment of up to 2048 rows is one bucket); then, when col
+ * (the CSR block lists, device int32, optional) is given, each bucket keeps
+ * the sorted order only if its consecutive rows share at least as many KV
+ * blocks as in the sequence order (the rows an XCD runs one after another
+ * reuse each other's K/V in L2), estimated with a 256-bit signature per row
+ * (bit v mod 256 of every listed block v): the cost of an order is the sum
+ * over its rows of the signature bits a row sets that the previous row does
+ * not (the first row: all of them), and the sequence order is kept when its
+ * cost is smaller.  head_step 1
  * schedules every row; head_step 2 only the rows of the first head of each
  * pair of query heads sharing a KV head (heads g*G + 2j), for the attention
  * path that serves a pair's identical rows in one launch (kv_share), and
@@ -353,8 +361,8 @@ int bsa_is_sample(const float *qbar, const float *kbar, const int32_t *q_seg_ptr
  * NULL pointers, non-positive sizes, Hq % Hkv != 0, head_step not 1 or 2 or
  * not dividing G.  Asynchronous.
  * ------------------------------------------------------------------------- */
-int bsa_schedule(const int32_t *row_ptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB, int32_t wave_rows,
-                 int32_t n_xcd, const int32_t *row_perm, int32_t head_step, int32_t *order,
+int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t B, int32_t Hq, int32_t Hkv, int32_t nQB,
+                 int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm, int32_t head_step, int32_t *order,
                  bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------

@@ -75,7 +75,7 @@ def lib():
         L.oracle_perm_from_labels.restype = ctypes.c_int
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
-        L.oracle_schedule.argtypes = [P, I64, I64, I64, I64, I64, I64, P, I64, P]
+        L.oracle_schedule.argtypes = [P, P, I64, I64, I64, I64, I64, I64, P, I64, P]
         L.oracle_spectral_order.restype = ctypes.c_int
         L.oracle_spectral_order.argtypes = [P, P, I64, I64, I64, I64, P, P]
         L.oracle_attn_rows.restype = ctypes.c_int
@@ -216,15 +216,19 @@ def perm_from_labels(labels: np.ndarray, n_clusters: int) -> np.ndarray:
 
 
 def schedule(row_ptr: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int, n_xcd: int = 1,
-             row_perm: Optional[np.ndarray] = None, head_step: int = 1):
+             row_perm: Optional[np.ndarray] = None, head_step: int = 1, col: Optional[np.ndarray] = None):
     """Launch order of the rows; with head_step 2 only the rows of the first
-    head of each pair of query heads sharing a KV head (B*Hq*nQB/2 rows)."""
+    head of each pair of query heads sharing a KV head (B*Hq*nQB/2 rows).
+    W = 0: buckets of 2048; with ``col`` given each keeps the sorted or the
+    sequence order, whichever shares more blocks between consecutive rows."""
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    if col is not None:
+        col = np.ascontiguousarray(col, dtype=np.int32)
     if row_perm is not None:
         row_perm = np.ascontiguousarray(row_perm, dtype=np.int32).reshape(-1)
         assert row_perm.size == B * Hq * nQB
     order = np.empty(B * Hq * nQB // head_step, dtype=np.int32)
-    rc = lib().oracle_schedule(_p(row_ptr), B, Hq, Hkv, nQB, W, n_xcd, _p(row_perm), head_step, _p(order))
+    rc = lib().oracle_schedule(_p(row_ptr), _p(col), B, Hq, Hkv, nQB, W, n_xcd, _p(row_perm), head_step, _p(order))
     if rc:
         raise ValueError("oracle_schedule failed: %d" % rc)
     return order

@@ -259,11 +259,36 @@ int oracle_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_
  * at most W consecutive entries within one (b, g) segment are sorted by
  * (nnz descending, sequence position ascending).  With n_xcd > 1 the list is
  * then dealt so that launch index i runs logical position start(i % n_xcd) +
- * i / n_xcd, where XCD x receives the x-th contiguous slice. */
-int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t nQB,
-                    int64_t W, int64_t n_xcd, const int32_t *row_perm, int64_t head_step, int32_t *order) {
-  if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W <= 0)
+ * i / n_xcd, where XCD x receives the x-th contiguous slice.
+ *
+ * W = 0 takes buckets of 2048 entries.  With W = 0 and the block lists (col)
+ * given, each bucket keeps whichever of two orders lets consecutive rows
+ * share more KV blocks (the rows an XCD runs one after another; WaveAlign,
+ * section IV: the schedule exists for K/V reuse in L2): the sorted order
+ * above, or the sequence order itself.  Shared blocks are estimated with a
+ * 256-bit signature per row (bit v mod 256 for every listed block v, v read
+ * as unsigned): the cost of an order is the sum over its rows of the bits
+ * set in a row's signature and not in the previous row's (the first row:
+ * all of its bits); the sequence order is kept when its cost is smaller. */
+static int sig_fresh(const uint64_t *a, const uint64_t *prev) {
+  int c = 0;
+  for (int w = 0; w < 4; ++w) {
+    uint64_t x = a[w] & ~(prev ? prev[w] : 0ull);
+    while (x) {
+      x &= x - 1;
+      ++c;
+    }
+  }
+  return c;
+}
+
+int oracle_schedule(const int32_t *row_ptr, const int32_t *col, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t nQB, int64_t W, int64_t n_xcd, const int32_t *row_perm, int64_t head_step,
+                    int32_t *order) {
+  if (!row_ptr || !order || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W < 0)
     return OR_ERR_ARG;
+  const int adaptive = W == 0 && col != NULL;
+  if (W == 0) W = 2048;
   if (head_step < 1 || (Hq / Hkv) % head_step) return OR_ERR_ARG;
   /* rows scheduled: heads g*G + j with j a multiple of head_step */
   int64_t G = Hq / Hkv, Gs = G / head_step, R = B * Hkv * Gs * nQB, seg = Gs * nQB;
@@ -279,6 +304,8 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
           int64_t uu = row_perm ? row_perm[h * nQB + u] : u;
           logical[pos++] = (int32_t)(h * nQB + uu);
         }
+  uint64_t *sig = adaptive ? (uint64_t *)calloc((size_t)W * 4, sizeof(uint64_t)) : NULL;
+  if (adaptive && !sig) return OR_ERR_ARG;
   for (int64_t s0 = 0; s0 < R; s0 += seg) {
     for (int64_t b0 = s0; b0 < s0 + seg; b0 += W) {
       int64_t n = (b0 + W <= s0 + seg) ? W : s0 + seg - b0;
@@ -288,6 +315,23 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
         buf[i].idx = (int32_t)i;
       }
       qsort(buf, (size_t)n, sizeof(key_idx), cmp_key_idx);
+      if (adaptive) {
+        for (int64_t i = 0; i < n; ++i) {
+          uint64_t *si = sig + 4 * i;
+          si[0] = si[1] = si[2] = si[3] = 0;
+          int32_t r = logical[b0 + i];
+          for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+            uint32_t bit = (uint32_t)col[e] % 256u;
+            si[bit / 64] |= 1ull << (bit % 64);
+          }
+        }
+        int64_t cost_sorted = 0, cost_seq = 0;
+        for (int64_t i = 0; i < n; ++i) {
+          cost_seq += sig_fresh(sig + 4 * i, i ? sig + 4 * (i - 1) : NULL);
+          cost_sorted += sig_fresh(sig + 4 * buf[i].idx, i ? sig + 4 * buf[i - 1].idx : NULL);
+        }
+        if (cost_seq < cost_sorted) continue;   /* keep the sequence order */
+      }
       int32_t tmp[4096];
       int32_t *t = n <= 4096 ? tmp : (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
       for (int64_t i = 0; i < n; ++i) t[i] = logical[b0 + buf[i].idx];
@@ -304,6 +348,7 @@ int oracle_schedule(const int32_t *row_ptr, int64_t B, int64_t Hq, int64_t Hkv, 
       order[i] = logical[start + k];
     }
   }
+  free(sig);
   free(buf);
   free(logical);
   return OR_OK;

@@ -82,13 +82,13 @@ def test_perm_argument_errors(L):
 
 
 def test_schedule_argument_errors(L):
-    assert L.bsa_schedule(None, 1, 4, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 6, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 4096, 8, FAKE, 1, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, -1, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 16, 8, None, 3, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_schedule(FAKE, 1, 4, 4, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 1
-    assert L.bsa_schedule(FAKE, 1, 6, 2, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 3
+    assert L.bsa_schedule(None, None, 1, 4, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, None, 1, 6, 4, 8, 16, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, None, 1, 4, 4, 8, 4096, 8, FAKE, 1, FAKE, None) == _lib.BSA_ERR_UNSUPPORTED
+    assert L.bsa_schedule(FAKE, None, 1, 4, 4, 8, -1, 8, None, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, None, 1, 4, 4, 8, 16, 8, None, 3, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_schedule(FAKE, None, 1, 4, 4, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 1
+    assert L.bsa_schedule(FAKE, None, 1, 6, 2, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 3
 
 
 def test_pair_rows_equal_argument_errors(L):

@@ -46,13 +46,13 @@ def test_config_parity(name):
     if pq is not None:
         assert np.array_equal(res.perm_q.cpu().numpy(), pq)
         assert np.array_equal(res.perm_k.cpu().numpy(), pk)
-    W = 2048   # wave_rows = 0 selects one bucket per segment of up to 2048 rows
+    W = 0   # one bucket per segment of up to 2048 rows, sorted or sequence order by shared blocks
     # the prefill pattern is the same for every head: the pipeline serves
     # query-head pairs in one launch, from a head-step-2 schedule
     assert res.kv_share == (name == "llm_prefill")
     hs = 2 if res.kv_share else 1
     assert np.array_equal(res.order.cpu().numpy(),
-                          oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8, head_step=hs))
+                          oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8, head_step=hs, col=col))
     _log("  integer steps bit-exact (nnz=%d)" % rp[-1])
     # stage-1 order of every head and the schedule built on it
     gp, ga = api.spectral_order(res.row_ptr, res.col, w.B * w.Hq, w.nQB, w.nQB, 10, want_angle=True)

@@ -100,7 +100,10 @@ def test_crm_attention_matches_oracle_and_csr(name):
     _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0)
     _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, crm=True)
     assert torch.equal(r_crm.row_ptr, r_csr.row_ptr)
-    assert torch.equal(r_crm.order, r_csr.order)
+    # the CSR launch table may take the sequence order (the schedule sees the
+    # lists); the CRM one sorts whole segments.  Outputs do not depend on it.
+    rp_np = r_csr.row_ptr.cpu().numpy()
+    assert np.array_equal(r_crm.order.cpu().numpy(), oracle.schedule(rp_np, w.B, w.Hq, w.Hkv, w.nQB, 0, 8))
     assert torch.equal(r_crm.out, r_csr.out)
     assert torch.equal(r_crm.lse, r_csr.lse)
     pq = pk = None

@@ -152,6 +152,35 @@ def test_schedule_bit_exact(B, Hq, Hkv, nQB, W, n_xcd):
     np.testing.assert_array_equal(got, oracle.schedule(row_ptr, B, Hq, Hkv, nQB, W, n_xcd))
 
 
+@pytest.mark.parametrize("kind,B,Hq,Hkv,nQB,n_xcd,hs,perm", [
+    ("random", 1, 4, 4, 37, 8, 1, False), ("banded", 2, 8, 2, 300, 8, 1, False),
+    ("clustered", 1, 6, 3, 591, 8, 1, False), ("banded", 1, 8, 2, 512, 8, 2, False),
+    ("mixed", 1, 4, 4, 700, 3, 1, True), ("random", 1, 2, 1, 1500, 8, 1, False)])
+def test_adaptive_schedule_bit_exact(kind, B, Hq, Hkv, nQB, n_xcd, hs, perm):
+    """wave_rows = 0 with the block lists: per segment the sorted or the
+    sequence order by the block signatures of consecutive rows (block indices
+    beyond 256 alias in the signature; both sides take the same bits)."""
+    rng = np.random.default_rng(nQB + Hq)
+    lists = []
+    for h in range(B * Hq):
+        for u in range(nQB):
+            if kind == "banded" or (kind == "mixed" and h % 2 == 0):
+                lists.append(list(range(max(0, u - 3), min(nQB, u + 4))))
+            elif kind in ("clustered", "mixed"):
+                c = (u * 7) % 5
+                lists.append(sorted(set(((97 * c + 3 * np.arange(6 + 4 * c)) % nQB).tolist())))
+            else:
+                lists.append(sorted(rng.choice(nQB, size=int(rng.integers(0, 30)), replace=False).tolist()))
+    row_ptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    col = np.concatenate([np.asarray(x, np.int32) for x in lists])
+    row_perm = np.stack([rng.permutation(nQB) for _ in range(B * Hq)]).astype(np.int32) if perm else None
+    _log("case adaptive schedule %s" % ((kind, B, Hq, Hkv, nQB, n_xcd, hs, perm),))
+    got = api.schedule(torch.from_numpy(row_ptr).cuda(), B, Hq, Hkv, nQB, 0, n_xcd, head_step=hs,
+                       col=torch.from_numpy(col).cuda(),
+                       row_perm=None if row_perm is None else torch.from_numpy(row_perm).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 0, n_xcd, row_perm, hs, col))
+
+
 def test_empty_rows_write_zero_and_minus_inf():
     w = synth.random_case(9, B=1, Hq=2, Hkv=2, N=300, d=128, block=128, density=0.0)
     w.force_diag = False

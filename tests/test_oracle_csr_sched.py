@@ -191,6 +191,72 @@ def test_schedule_of_head_pairs_matches_brute_force(B, Hq, Hkv, nQB, W, n_xcd):
         oracle.schedule(row_ptr[:B * 3 * nQB + 1], B, 3, 1, nQB, W, n_xcd, head_step=2)
 
 
+def _csr(lists):
+    row_ptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    col = np.concatenate([np.asarray(x, np.int32) for x in lists]) if row_ptr[-1] else np.zeros(1, np.int32)
+    return row_ptr, col
+
+
+def _adaptive_brute(row_ptr, col, B, Hq, Hkv, nQB, n_xcd, head_step=1):
+    """Per KV-group segment (nQB * G / head_step <= 2048 rows here): the
+    sorted order or the sequence order, whichever has the smaller sum of
+    |blocks of a row - blocks of the previous row| (exact sets: every block
+    index below 256, so the signature is exact); the sequence order wins only
+    when strictly smaller."""
+    G = Hq // Hkv
+    srt = sched_brute(row_ptr, B, Hq, Hkv, nQB, 2048, 1, head_step=head_step)
+    seq = sched_brute(row_ptr, B, Hq, Hkv, nQB, 1, 1, head_step=head_step)
+    seg = nQB * G // head_step
+    rows = [set(col[row_ptr[r]:row_ptr[r + 1]].tolist()) for r in range(len(row_ptr) - 1)]
+
+    def cost(o):
+        c, prev = 0, set()
+        for r in o:
+            c += len(rows[r] - prev)
+            prev = rows[r]
+        return c
+    logical = []
+    for s in range(0, len(srt), seg):
+        a, b = srt[s:s + seg], seq[s:s + seg]
+        logical += list(b if cost(b) < cost(a) else a)
+    R = len(logical)
+    if n_xcd <= 1:
+        return np.array(logical, np.int32)
+    counts = [len(range(x, R, n_xcd)) for x in range(n_xcd)]
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    return np.array([logical[starts[i % n_xcd] + i // n_xcd] for i in range(R)], np.int32)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nQB,n_xcd,hs,kind", [
+    (1, 4, 4, 37, 8, 1, "random"), (2, 8, 2, 40, 8, 1, "banded"), (1, 6, 3, 60, 3, 1, "clustered"),
+    (1, 8, 2, 50, 8, 2, "banded"), (2, 4, 1, 33, 1, 2, "random"), (1, 2, 2, 70, 8, 1, "mixed")])
+def test_adaptive_bucket_order_matches_set_differences(B, Hq, Hkv, nQB, n_xcd, hs, kind):
+    """Schedule with W = 0 and the lists: each segment keeps the order whose
+    consecutive rows share more blocks, against exact set differences."""
+    rng = np.random.default_rng(nQB + 17 * Hq)
+    lists = []
+    for h in range(B * Hq):
+        for u in range(nQB):
+            if kind == "banded" or (kind == "mixed" and h % 2 == 0):
+                lists.append(list(range(max(0, u - 2), min(nQB, u + 3))))
+            elif kind == "clustered" or kind == "mixed":
+                c = (u * 7) % 4   # cluster of the row, interleaved along the sequence
+                lists.append(sorted(set((40 * c + np.arange(5 + 3 * c)).tolist())))
+            else:
+                lists.append(sorted(rng.choice(200, size=int(rng.integers(0, 12)), replace=False).tolist()))
+    row_ptr, col = _csr(lists)
+    got = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 0, n_xcd, head_step=hs, col=col)
+    np.testing.assert_array_equal(got, _adaptive_brute(row_ptr, col, B, Hq, Hkv, nQB, n_xcd, hs))
+    srt = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 2048, n_xcd, head_step=hs)
+    seq = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 1, n_xcd, head_step=hs)
+    if kind == "banded":        # neighbours share four of five blocks: the sequence order is kept
+        np.testing.assert_array_equal(got, seq)
+    if kind == "clustered":     # equal-length rows of one cluster share every block: sorted
+        np.testing.assert_array_equal(got, srt)
+    # without the lists W = 0 is one sorted bucket per segment
+    np.testing.assert_array_equal(oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 0, n_xcd, head_step=hs), srt)
+
+
 def test_schedule_buckets_longest_first():
     rng = np.random.default_rng(3)
     B, Hq, Hkv, nQB, W = 1, 6, 6, 64, 10
