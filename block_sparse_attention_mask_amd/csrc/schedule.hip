@@ -80,11 +80,23 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
       kk = ((uint64_t)(uint32_t)(0x7fffffff - nnz) << 32) | (uint32_t)i;
       if (col) {
         uint64_t sg[4] = {0, 0, 0, 0};
-        if (r >= 0)
-          for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
-            const uint32_t bit = (uint32_t)col[e] & 255u;
-            sg[bit >> 6] |= 1ull << (bit & 63);
+        auto add = [&](int32_t v) {
+          const uint32_t bit = (uint32_t)v & 255u;
+          sg[bit >> 6] |= 1ull << (bit & 63);
+        };
+        if (r >= 0) {
+          const int32_t e1 = row_ptr[r + 1];
+          int32_t e = row_ptr[r];
+          // eight independent loads in flight per step
+          for (; e + 8 <= e1; e += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = col[e + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) add(v[j]);
           }
+          for (; e < e1; ++e) add(col[e]);
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w) sig[i][w] = sg[w];
       }
