@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--selection-only", action="store_true",
                     help="instead of the step: run only the exact-selection (anchor step) measurements, "
                          "print them as one JSON line, and exit")
+    ap.add_argument("--token-sets-only", action="store_true",
+                    help="instead of the step: run only the token-level set measurements and print them")
     ap.add_argument("--n-xcd", type=int, default=8)
     ap.add_argument("--wave-rows", type=int, default=0)
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -121,6 +123,9 @@ def main():
         return
     if args.selection_only:
         print(json.dumps({"exact_selection": selection_stage(torch)}), flush=True)
+        return
+    if args.token_sets_only:
+        print(json.dumps({"token_sets": token_set_stage(torch)}), flush=True)
         return
 
     t0 = time.time()
