@@ -22,11 +22,14 @@
 //     2j + 3.  So each phase stages one half tile (K in even phases, V^T in
 //     odd ones), half of what a one-head workgroup stages per unit of work.
 //     K(j) is copied in phase 2j - 4 into K buffer j % 3, V^T(j) in phase
-//     2j - 1 into V^T buffer j % 3: a copy has three phases to land and a
-//     buffer is refilled only after both heads have read it.  The softmax
-//     step of the phase issues the copies (head 1's E(j) copies K(j + 3),
-//     head 0's E(j) copies V^T(j + 1)); M steps issue only LDS reads and
-//     MFMAs.
+//     2j - 1 into V^T buffer j % 3, and a buffer is refilled only after both
+//     heads have read it.  The softmax step of the phase issues the copies
+//     (head 1's E(j) copies K(j + 3), head 0's E(j) copies V^T(j + 1)); M
+//     steps issue only LDS reads and MFMAs.  A wavefront waits, at the end of
+//     each phase, for every copy it issued before its latest softmax step,
+//     so a copy has landed by the end of the second phase after the one
+//     that issued it (before phase 2j - 1 for K(j), first read in phase 2j;
+//     before phase 2j + 2 for V^T(j), first read in phase 2j + 2).
 //   * LDS layout, MFMA mapping, swizzle, list staging and the fixed-max
 //     passes (a row whose probability total overflows 2^64 or stays below
 //     2^-60 is recomputed from its cold tiles' max) are those of attn_pp.hip.
