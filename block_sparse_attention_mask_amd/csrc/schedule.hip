@@ -30,7 +30,11 @@
 // other's K/V in its L2): sorting by length groups the rows of one cluster of
 // a permuted head, but scatters the neighbouring rows of a banded or local
 // pattern.  Shared blocks are estimated with a 256-bit signature per row (bit
-// v mod 256 of each listed block v), kept in LDS.
+// v mod 256 of each listed block v), kept in LDS.  When the sequence order
+// wins, it is sorted longest-first within windows of kSeqWave consecutive
+// rows (WaveAlign's intra-wave alignment, section IV-D, over a window of two
+// XCD-waves of rows), which keeps neighbours together and balances each
+// window.
 //
 // bsa_pair_rows_equal checks the precondition of that pair kernel: one
 // wavefront per pair of rows compares lengths, block indices and log-weight
@@ -40,6 +44,7 @@
 namespace {
 
 constexpr int kMaxWave = 2048;
+constexpr int kSeqWave = 64;   // rows per longest-first window of a sequence-order bucket
 
 __device__ __forceinline__ int sig_fresh(const uint64_t *a, const uint64_t *prev) {
   int c = 0;
@@ -105,21 +110,24 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   }
   if (threadIdx.x < 2) cost[threadIdx.x] = 0;
   __syncthreads();
-  for (int size = 2; size <= P2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < P2 / 2; i += 1024) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = key[lo], c = key[hi];
-        if ((a > c) == up) {
-          key[lo] = c;
-          key[hi] = a;
+  auto sort_keys = [&]() {
+    for (int size = 2; size <= P2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = threadIdx.x; i < P2 / 2; i += 1024) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t a = key[lo], c = key[hi];
+          if ((a > c) == up) {
+            key[lo] = c;
+            key[hi] = a;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
+  };
+  sort_keys();
   bool keep_seq = false;
   if (col) {
     int cs = 0, cq = 0;
@@ -132,9 +140,25 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
     atomicAdd(&cost[1], cq);
     __syncthreads();
     keep_seq = cost[1] < cost[0];
+    if (keep_seq) {
+      // sequence order, longest-first within each window of kSeqWave rows:
+      // keys (window, INT32_MAX - nnz, position) in 5 + 31 + 12 bits
+      __syncthreads();
+      for (int i = threadIdx.x; i < P2; i += 1024) {
+        uint64_t kk = ~0ull;
+        if (i < n) {
+          const int64_t r = row_at(k * W + i);
+          const int32_t nnz = r >= 0 ? row_ptr[r + 1] - row_ptr[r] : 0;
+          kk = ((uint64_t)(i / kSeqWave) << 43) | ((uint64_t)(uint32_t)(0x7fffffff - nnz) << 12) | (uint32_t)i;
+        }
+        key[i] = kk;
+      }
+      __syncthreads();
+      sort_keys();
+    }
   }
   for (int i = threadIdx.x; i < n; i += 1024) {
-    const int src = keep_seq ? i : (int)(key[i] & 0xffffffffu);
+    const int src = (int)(key[i] & (keep_seq ? 0xfffu : 0xffffffffu));
     const int32_t r = (int32_t)row_at(k * W + src);
     const int64_t P = start + i;                    // logical position
     int64_t launch = P;

@@ -269,7 +269,10 @@ int oracle_perm_from_labels(const int32_t *labels, int64_t BH, int64_t N, int32_
  * 256-bit signature per row (bit v mod 256 for every listed block v, v read
  * as unsigned): the cost of an order is the sum over its rows of the bits
  * set in a row's signature and not in the previous row's (the first row:
- * all of its bits); the sequence order is kept when its cost is smaller. */
+ * all of its bits); the sequence order is kept when its cost is smaller,
+ * and then sorted by (nnz descending, position ascending) within each window
+ * of 64 consecutive entries of the bucket (WaveAlign's intra-wave alignment
+ * over two XCD-waves of rows). */
 static int sig_fresh(const uint64_t *a, const uint64_t *prev) {
   int c = 0;
   for (int w = 0; w < 4; ++w) {
@@ -330,7 +333,21 @@ int oracle_schedule(const int32_t *row_ptr, const int32_t *col, int64_t B, int64
           cost_seq += sig_fresh(sig + 4 * i, i ? sig + 4 * (i - 1) : NULL);
           cost_sorted += sig_fresh(sig + 4 * buf[i].idx, i ? sig + 4 * buf[i - 1].idx : NULL);
         }
-        if (cost_seq < cost_sorted) continue;   /* keep the sequence order */
+        if (cost_seq < cost_sorted) {   /* the sequence order, sorted within windows of 64 */
+          for (int64_t w0 = 0; w0 < n; w0 += 64) {
+            int64_t m = w0 + 64 <= n ? 64 : n - w0;
+            for (int64_t i = 0; i < m; ++i) {
+              int32_t r = logical[b0 + w0 + i];
+              buf[i].key = -(int64_t)(row_ptr[r + 1] - row_ptr[r]);
+              buf[i].idx = (int32_t)i;
+            }
+            qsort(buf, (size_t)m, sizeof(key_idx), cmp_key_idx);
+            int32_t t[64];
+            for (int64_t i = 0; i < m; ++i) t[i] = logical[b0 + w0 + buf[i].idx];
+            memcpy(&logical[b0 + w0], t, sizeof(int32_t) * (size_t)m);
+          }
+          continue;
+        }
       }
       int32_t tmp[4096];
       int32_t *t = n <= 4096 ? tmp : (int32_t *)malloc(sizeof(int32_t) * (size_t)n);

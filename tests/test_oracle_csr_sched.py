@@ -202,10 +202,12 @@ def _adaptive_brute(row_ptr, col, B, Hq, Hkv, nQB, n_xcd, head_step=1):
     sorted order or the sequence order, whichever has the smaller sum of
     |blocks of a row - blocks of the previous row| (exact sets: every block
     index below 256, so the signature is exact); the sequence order wins only
-    when strictly smaller."""
+    when strictly smaller, and is then emitted sorted within 64-row windows
+    (the fixed 64-row buckets)."""
     G = Hq // Hkv
     srt = sched_brute(row_ptr, B, Hq, Hkv, nQB, 2048, 1, head_step=head_step)
     seq = sched_brute(row_ptr, B, Hq, Hkv, nQB, 1, 1, head_step=head_step)
+    win = sched_brute(row_ptr, B, Hq, Hkv, nQB, 64, 1, head_step=head_step)
     seg = nQB * G // head_step
     rows = [set(col[row_ptr[r]:row_ptr[r + 1]].tolist()) for r in range(len(row_ptr) - 1)]
 
@@ -218,7 +220,7 @@ def _adaptive_brute(row_ptr, col, B, Hq, Hkv, nQB, n_xcd, head_step=1):
     logical = []
     for s in range(0, len(srt), seg):
         a, b = srt[s:s + seg], seq[s:s + seg]
-        logical += list(b if cost(b) < cost(a) else a)
+        logical += list(win[s:s + seg] if cost(b) < cost(a) else a)
     R = len(logical)
     if n_xcd <= 1:
         return np.array(logical, np.int32)
@@ -248,8 +250,8 @@ def test_adaptive_bucket_order_matches_set_differences(B, Hq, Hkv, nQB, n_xcd, h
     got = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 0, n_xcd, head_step=hs, col=col)
     np.testing.assert_array_equal(got, _adaptive_brute(row_ptr, col, B, Hq, Hkv, nQB, n_xcd, hs))
     srt = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 2048, n_xcd, head_step=hs)
-    seq = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 1, n_xcd, head_step=hs)
-    if kind == "banded":        # neighbours share four of five blocks: the sequence order is kept
+    seq = oracle.schedule(row_ptr, B, Hq, Hkv, nQB, 64, n_xcd, head_step=hs)
+    if kind == "banded":        # neighbours share four of five blocks: the sequence order, in 64-row windows
         np.testing.assert_array_equal(got, seq)
     if kind == "clustered":     # equal-length rows of one cluster share every block: sorted
         np.testing.assert_array_equal(got, srt)
