@@ -379,12 +379,15 @@ __device__ __forceinline__ void attn_pp_body(const AttnParams &p, const int32_t 
     constexpr int VM0 = KH ? VY0 : VX0, VM1 = KH ? VY1 : VX1;
     auto m_phase = [&](int j, auto par) -> Pre {
       constexpr int P = decltype(par)::value;   // j & 1
-      const Pre pr = pre_of(j);
       // the matrix step issues ahead of the softmax step of the SIMD's other
       // wavefront: its MFMAs and operand reads are not held up behind VALU work
       __builtin_amdgcn_s_setprio(1);
       mstep(smem + (P ? VM0 : VM1) * C::KB, smem + (P ? KM1 : KM0) * C::KB);
       __builtin_amdgcn_s_setprio(0);
+      // the next softmax step's list reads come after every MFMA has issued:
+      // their waits would otherwise hold up the first operand reads
+      __builtin_amdgcn_sched_barrier(0);
+      const Pre pr = pre_of(j);
       pin_results();
       end_phase();
       return pr;

@@ -308,12 +308,15 @@ __device__ __forceinline__ void attn_ppg_body(const AttnParams &p, const int32_t
     // E(j) copies into V^T buffer (j + 1) % 3 (head 0) or K buffer j % 3 (head 1)
     auto m_phase = [&](int j, auto kc) -> Pre {
       constexpr int K3 = decltype(kc)::value;   // j % 3
-      const Pre pr = pre_of(j);
       // the matrix step issues ahead of the softmax step of the SIMD's other
       // wavefront: its MFMAs and operand reads are not held up behind VALU work
       __builtin_amdgcn_s_setprio(1);
       mstep(smem + (3 + (K3 + 2) % 3) * C::KB, smem + K3 * C::KB);
       __builtin_amdgcn_s_setprio(0);
+      // the next softmax step's list reads come after every MFMA has issued:
+      // their waits would otherwise hold up the first operand reads
+      __builtin_amdgcn_sched_barrier(0);
+      const Pre pr = pre_of(j);
       pin_results();
       end_phase();
       return pr;
