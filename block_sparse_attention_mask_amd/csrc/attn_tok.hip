@@ -111,11 +111,18 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   // the set whose slots and list this workgroup reads: set i, or with two
   // heads the i-th set of an even head (its partner head's set is identical)
   // (set counts are below 2^31: 32-bit index arithmetic)
+  // Workgroups are dispatched round-robin over the 8 XCDs; unit i (set, or
+  // pair of sets) goes to the workgroup that makes XCD x run the x-th
+  // contiguous share of the units, so that the sets an XCD runs at the same
+  // time are neighbours, which list mostly the same keys, and its L2 holds
+  // their K and V rows.
+  const int nu = (int)gridDim.x, xcd = (int)(blockIdx.x & 7);
+  const int i = xcd * (nu >> 3) + (xcd < (nu & 7) ? xcd : (nu & 7)) + (int)(blockIdx.x >> 3);
   int set0;
   if (HP == 1) {
-    set0 = (int)blockIdx.x;
+    set0 = i;
   } else {
-    const int i = (int)blockIdx.x, pr = i / p.sets;
+    const int pr = i / p.sets;
     set0 = (2 * pr) * p.sets + (i - pr * p.sets);
   }
   if (set0 >= p.n_sets) return;
