@@ -132,14 +132,25 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   const int g = h / p.G;
   const int N = p.N;
   const int e0 = p.kv_ptr[set0], e1 = p.kv_ptr[set0 + 1];
+  // the first chunk of the list goes to registers at once: its loads then
+  // overlap the query loads below instead of following them
+  constexpr int PF = C::LIST / C::NT;
+  int32_t pre[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int i = tid + C::NT * k;
+    pre[k] = i < e1 - e0 ? p.kv_idx[e0 + i] : -1;
+  }
 
-  // this lane's query and the set's first query (for the causal flags)
+  // this lane's query and, when causal, the set's first query (for the flags)
   const int32_t qraw = p.q_idx[(int64_t)set0 * BQ + qg * 32 + ln];
   const bool qok = qraw >= 0 && qraw < N;
   const int qi = qok ? qraw : -1;
-  if (tid == 0) qmin_s = 0x7fffffff;
-  __syncthreads();
-  if (kh == 0 && hd == 0 && qok) atomicMin(&qmin_s, qi);
+  if (p.causal) {
+    if (tid == 0) qmin_s = 0x7fffffff;
+    __syncthreads();
+    if (kh == 0 && hd == 0 && qok) atomicMin(&qmin_s, qi);
+  }
 
   const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((int64_t)(N - 1) * p.qs2 + D) * 2);
   const i32x4 krs = buffer_rsrc(p.k + b * p.ks0 + g * p.ks1, ((int64_t)(N - 1) * p.ks2 + D) * 2);
@@ -292,17 +303,34 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
       }
   };
 
+  // Staging of a list chunk of n entries: the tile flags start as "partial
+  // last tile"; an entry outside the sequence or, when causal, after the
+  // set's first query flags its tile.
+  int qmin = 0;
+  auto flags_init = [&]() {
+    const int nt = (n + C::BK - 1) / C::BK;
+    if (tid < C::NTL) tflag[tid] = (tid == nt - 1 && (n % C::BK)) ? 1 : 0;
+  };
+  auto put = [&](int i, int kp) {
+    lcol[i] = kp;
+    if (kp < 0 || kp >= N || (p.causal && kp > qmin)) atomicOr(&tflag[i / C::BK], 1);
+  };
+  // the first chunk from the registers, before the chunk loop, so that they
+  // are free during it
+  n = e1 - e0 < C::LIST ? e1 - e0 : C::LIST;
+  flags_init();
   __syncthreads();
-  const int qmin = qmin_s;
+  if (p.causal) qmin = qmin_s;
+#pragma unroll
+  for (int k = 0; k < PF; ++k)
+    if (tid + C::NT * k < n) put(tid + C::NT * k, pre[k]);
   for (int c0 = e0; c0 < e1; c0 += C::LIST) {
     n = e1 - c0 < C::LIST ? e1 - c0 : C::LIST;
     const int nt = (n + C::BK - 1) / C::BK;
-    if (tid < C::NTL) tflag[tid] = (tid == nt - 1 && (n % C::BK)) ? 1 : 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += C::NT) {
-      const int kp = p.kv_idx[c0 + i];
-      lcol[i] = kp;
-      if (kp < 0 || kp >= N || (p.causal && kp > qmin)) atomicOr(&tflag[i / C::BK], 1);
+    if (c0 != e0) {
+      flags_init();
+      __syncthreads();
+      for (int i = tid; i < n; i += C::NT) put(i, p.kv_idx[c0 + i]);
     }
     __syncthreads();
     // prologue: K(0), V(0), K(1) resident, then S(0)
