@@ -470,8 +470,11 @@ def token_set_stage(torch):
           *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
     # the same sets served per pair of query heads of a KV group (the map is
     # the same for every head): each gathered K/V tile serves both heads
-    timed("intra_scatter_llama3_8b_32k_head_pairs", "same, one launch per pair of query heads sharing a KV head",
+    timed("intra_scatter_llama3_8b_32k_head_pairs", "same, one workgroup per pair of query heads sharing a KV head",
           *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=True)
+    # ... and per run of the four query heads of a KV head (GQA-4)
+    timed("intra_scatter_llama3_8b_32k_head_quads", "same, one workgroup per four query heads sharing a KV head",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=4)
     # the same pattern executed as 128-query sets (two consecutive 64-query
     # sets of a group share the later one's key list; causal masking keeps
     # the computation identical)
@@ -482,8 +485,10 @@ def token_set_stage(torch):
     maps = synth.cqs_per_head(synth.cqs_gather1(N, R, 64, True), Hq)
     timed("intra_gather1_llama3_8b_32k", "1x32q/8kv x 32768, d128, 8 groups of cyclic 8-token segments, causal, "
           "64-query sets", *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs)
-    timed("intra_gather1_llama3_8b_32k_head_pairs", "same, one launch per pair of query heads sharing a KV head",
+    timed("intra_gather1_llama3_8b_32k_head_pairs", "same, one workgroup per pair of query heads sharing a KV head",
           *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=True)
+    timed("intra_gather1_llama3_8b_32k_head_quads", "same, one workgroup per four query heads sharing a KV head",
+          *qkv_s, *(torch.from_numpy(x).to(dev) for x in maps), True, pairs, kv_share=4)
     del qkv_s
     # INTRA Gather 0, FLUX.1-dev 2048x2048 image (128x128 tokens): 8x8 patches, 16x16 windows
     H = W = 128

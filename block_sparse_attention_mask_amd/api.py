@@ -450,15 +450,16 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
 
 def attn_tok_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, kv_ptr: torch.Tensor,
                  kv_idx: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 want_lse: bool = False, scale: float = 0.0, causal: bool = False, kv_share: bool = False,
+                 want_lse: bool = False, scale: float = 0.0, causal: bool = False, kv_share=False,
                  stream=None):
     """Token-level attention over computational query sets: q_idx int32
     [B*Hq][n_sets][set_size] query positions, kv_ptr int32 [B*Hq*n_sets + 1]
     and kv_idx int32 key positions; q, k, v token-major.  Returns (out, lse).
     Rows of out at positions no set lists are left as they were (out is
-    zero-filled when allocated here).  With ``kv_share`` the sets of query
-    heads 2j and 2j + 1 of every KV group must be identical: one launch
-    serves both heads, gathering each K/V tile once."""
+    zero-filled when allocated here).  With ``kv_share`` (True or 2, or 4)
+    the sets of each run of 2 (or 4) consecutive query heads of a KV group
+    must be identical: one launch serves them all, gathering each K/V tile
+    once for them."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     for t, n in ((q_idx, "q_idx"), (kv_ptr, "kv_ptr"), (kv_idx, "kv_idx")):
@@ -484,7 +485,7 @@ def attn_tok_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch
     a.q_idx, a.kv_ptr, a.kv_idx = _ptr(q_idx), _ptr(kv_ptr), _ptr(kv_idx)
     a.scale = float(scale)
     a.causal = int(bool(causal))
-    a.kv_share = 2 if kv_share else 0
+    a.kv_share = 0 if not kv_share else (2 if kv_share is True else int(kv_share))
     check("bsa_attn_tok_fwd", load().bsa_attn_tok_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse
 

@@ -123,7 +123,7 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     set0 = i;
   } else {
     const int pr = i / p.sets;
-    set0 = (2 * pr) * p.sets + (i - pr * p.sets);
+    set0 = (HP * pr) * p.sets + (i - pr * p.sets);
   }
   if (set0 >= p.n_sets) return;
   const int bh = set0 / p.sets + hd;   // this wavefront's head
@@ -411,14 +411,15 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
 // 128-query sets and pairs of 64-query sets: 4 wavefronts that each take
 // whole tiles, two per CU
 #define BSA_TOK_KERNEL(NAME, BQ, HP, KSPLIT)                                                        \
-  __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))      \
+  __global__ __attribute__((amdgpu_flat_work_group_size(TCfg<BQ, HP, KSPLIT>::NT, TCfg<BQ, HP, KSPLIT>::NT), \
+                            amdgpu_waves_per_eu(2, 2)))                                             \
   void NAME(const TokParams p) {                                                                   \
-    static_assert(TCfg<BQ, HP, KSPLIT>::NT == 256, "four wavefronts");                             \
     attn_tok_body<BQ, HP, KSPLIT>(p);                                                               \
   }
 BSA_TOK_KERNEL(attn_tok_64, 64, 1, 2)
 BSA_TOK_KERNEL(attn_tok_128, 128, 1, 1)
 BSA_TOK_KERNEL(attn_tok_64x2, 64, 2, 1)
+BSA_TOK_KERNEL(attn_tok_64x4, 64, 4, 1)
 #undef BSA_TOK_KERNEL
 
 bool bad_strides(const int64_t s[3]) {
@@ -437,8 +438,8 @@ extern "C" int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream) {
   if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->N <= 0 || a->n_sets < 0) return BSA_ERR_ARG;
   if (a->Hq % a->Hkv) return BSA_ERR_ARG;
   if (a->d != 128 || (a->set_size != 64 && a->set_size != 128)) return BSA_ERR_UNSUPPORTED;
-  if (a->kv_share != 0 && a->kv_share != 2) return BSA_ERR_ARG;
-  if (a->kv_share == 2 && (a->set_size != 64 || (a->Hq / a->Hkv) % 2)) return BSA_ERR_UNSUPPORTED;
+  if (a->kv_share != 0 && a->kv_share != 2 && a->kv_share != 4) return BSA_ERR_ARG;
+  if (a->kv_share && (a->set_size != 64 || (a->Hq / a->Hkv) % a->kv_share)) return BSA_ERR_UNSUPPORTED;
   if (!bsa_aligned16(a->q) || !bsa_aligned16(a->k) || !bsa_aligned16(a->v) || !bsa_aligned16(a->o))
     return BSA_ERR_ARG;
   if (tok::bad_strides(a->q_str) || tok::bad_strides(a->k_str) || tok::bad_strides(a->v_str) ||
@@ -476,7 +477,8 @@ extern "C" int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream) {
   const float scale = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->d);
   p.c = scale * kLog2e;
   hipStream_t s = bsa_hip_stream(stream);
-  if (a->kv_share == 2) hipLaunchKernelGGL(tok::attn_tok_64x2, dim3((unsigned)(n_sets / 2)), dim3(256), 0, s, p);
+  if (a->kv_share == 4) hipLaunchKernelGGL(tok::attn_tok_64x4, dim3((unsigned)(n_sets / 4)), dim3(512), 0, s, p);
+  else if (a->kv_share == 2) hipLaunchKernelGGL(tok::attn_tok_64x2, dim3((unsigned)(n_sets / 2)), dim3(256), 0, s, p);
   else if (a->set_size == 64) hipLaunchKernelGGL(tok::attn_tok_64, dim3((unsigned)n_sets), dim3(256), 0, s, p);
   else hipLaunchKernelGGL(tok::attn_tok_128, dim3((unsigned)n_sets), dim3(256), 0, s, p);
   BSA_LAUNCH_CHECK();

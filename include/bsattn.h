@@ -480,13 +480,15 @@ int bsa_pair_rows_equal(const int32_t *row_ptr, const int32_t *col, const float 
  * alias q, k or v.  d must be 128 (BSA_ERR_UNSUPPORTED otherwise, and for
  * set_size outside {64, 128} or larger extents); BSA_ERR_ARG for NULL
  * pointers, non-positive sizes, Hq % Hkv != 0 or misaligned strides.
- * scale <= 0 selects 1/sqrt(d).  kv_share: 0, or 2 when query heads 2j and
- * 2j + 1 of every KV-head group have identical sets (same query slots, same
- * key lists; INTRA's Scatter and Gather maps hold for every head): then one
- * launch serves both heads' sets, gathering each K/V tile once for both;
- * the sets of head 2j + 1 are not read.  Requires set_size = 64 and
- * Hq / Hkv even (else BSA_ERR_UNSUPPORTED); results equal those of
- * kv_share = 0 on sets that meet the precondition.  Asynchronous.
+ * scale <= 0 selects 1/sqrt(d).  kv_share: 0, or s = 2 or 4 when every run
+ * of s consecutive query heads s j .. s j + s - 1 of a KV-head group has
+ * identical sets (same query slots, same key lists; INTRA's Scatter and
+ * Gather maps hold for every head): then one workgroup serves the run's
+ * sets, gathering each K/V tile once for all s heads; only the sets of head
+ * s j are read.  Requires set_size = 64 and Hq / Hkv a multiple of s (else
+ * BSA_ERR_UNSUPPORTED; other values BSA_ERR_ARG); results equal those of
+ * kv_share = 0 on sets that meet the precondition, up to rounding order.
+ * Asynchronous.
  * ------------------------------------------------------------------------- */
 typedef struct {
   const void *q, *k, *v;
@@ -499,7 +501,7 @@ typedef struct {
   const int32_t *q_idx, *kv_ptr, *kv_idx;
   float scale;
   int32_t causal;
-  int32_t kv_share; /* 0, or 2: heads 2j and 2j + 1 of a KV group have identical sets */
+  int32_t kv_share; /* 0, or 2 or 4: runs of that many heads of a KV group have identical sets */
 } bsa_tok_args;
 
 int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream);

@@ -186,6 +186,9 @@ def _tok_args(**kw):
     (dict(kv_share=1), _lib.BSA_ERR_ARG),
     (dict(kv_share=2, set_size=128), _lib.BSA_ERR_UNSUPPORTED),
     (dict(kv_share=2, Hkv=4), _lib.BSA_ERR_UNSUPPORTED),                                   # G = 1: no pairs
+    (dict(kv_share=3), _lib.BSA_ERR_ARG),
+    (dict(kv_share=4), _lib.BSA_ERR_UNSUPPORTED),                                          # G = 2: no quads
+    (dict(kv_share=4, Hq=8, Hkv=2, set_size=128), _lib.BSA_ERR_UNSUPPORTED),
 ])
 def test_attn_tok_argument_errors(L, kw, code):
     a = _tok_args(**kw)

@@ -6,10 +6,10 @@ Cases: random sets with lists of every awkward length (empty, 1, 63, 64,
 65, over a 1024- and a 2048-entry staging chunk), out-of-range and duplicate
 entries, empty query slots, GQA, full and causal masking, 64- and 128-query
 sets; INTRA's Scatter, Gather 1 and Gather 0 maps; a token-selection workload
-of MC-Sparse's shape.  The head-pair launch (kv_share: the sets of query
-heads 2j and 2j + 1 of a KV group are identical, each gathered tile serves
-both) is checked against the oracle and, within the same bar, against the
-per-head launch.  Bar: max-abs 2e-2, mean-abs 2e-3 on O, 1e-3 on LSE; rows that no set
+of MC-Sparse's shape.  The head-pair and head-quad launches (kv_share 2 or
+4: the sets of each run of 2 or 4 consecutive query heads of a KV group are
+identical, each gathered tile serves them all) are checked against the
+oracle and, within the same bar, against the per-head launch.  Bar: max-abs 2e-2, mean-abs 2e-3 on O, 1e-3 on LSE; rows that no set
 lists stay untouched.
 """
 import numpy as np
@@ -47,7 +47,7 @@ def _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, label, slots=None, 
     torch.cuda.synchronize()
     if kv_share:
         # the per-head launch splits every tile's keys over two wavefronts and
-        # merges them at the end; the pair launch walks whole tiles: same
+        # merges them at the end; the shared launches walk whole tiles: same
         # values up to rounding order
         ref_out, ref_lse = api.attn_tok_fwd(*args, want_lse=True, causal=causal)
         torch.cuda.synchronize()
@@ -132,22 +132,25 @@ def test_intra_gather1(causal):
     _run_and_compare(q, k, v, *maps, causal, "gather1")
 
 
-def _pair_identical_sets(g, B, Hq, N, C, BQ, lens):
-    """Random sets drawn per even head and copied to its partner head."""
+def _pair_identical_sets(g, B, Hq, N, C, BQ, lens, run=2):
+    """Random sets drawn per run of `run` consecutive heads (its first head)
+    and copied to the run's other heads."""
     q_idx = np.full((B * Hq, C, BQ), -1, np.int32)
     lists = [None] * (B * Hq * C)
-    for h in range(0, B * Hq, 2):
+    for h in range(0, B * Hq, run):
         pos = g.permutation(N)[:C * BQ - 5]
         flat = np.full(C * BQ, -1, np.int32)
         flat[g.permutation(C * BQ)[:len(pos)]] = pos
-        q_idx[h] = q_idx[h + 1] = flat.reshape(C, BQ)
+        for r in range(run):
+            q_idx[h + r] = flat.reshape(C, BQ)
         for c in range(C):
             keys = g.integers(0, N, size=lens[c]).astype(np.int32)
             if lens[c] > 10:
                 keys[3] = -1
                 keys[4] = N + 7
                 keys[5] = keys[6]
-            lists[h * C + c] = lists[(h + 1) * C + c] = keys
+            for r in range(run):
+                lists[(h + r) * C + c] = keys
     kv_ptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
     return q_idx, kv_ptr, np.concatenate(lists).astype(np.int32)
 
@@ -161,6 +164,27 @@ def test_head_pairs_random_sets(causal, Hq, Hkv):
     q_idx, kv_ptr, kv_idx = _pair_identical_sets(g, B, Hq, N, C, BQ, lens)
     _log("case tok head pairs random causal=%d Hq=%d Hkv=%d" % (causal, Hq, Hkv))
     _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, "head pairs", kv_share=True)
+
+
+@pytest.mark.parametrize("causal,Hq,Hkv", [(False, 4, 1), (True, 8, 2)])
+def test_head_quads_random_sets(causal, Hq, Hkv):
+    B, N, C, BQ = 1, 5000, 10, 64
+    q, k, v = _qkv(80 + causal + Hq, B, Hq, Hkv, N)
+    g = np.random.default_rng(81 + Hq)
+    lens = np.array([0, 1, 63, 64, 65, 300, 2100, 7, 129, 2048])
+    q_idx, kv_ptr, kv_idx = _pair_identical_sets(g, B, Hq, N, C, BQ, lens, run=4)
+    _log("case tok head quads random causal=%d Hq=%d Hkv=%d" % (causal, Hq, Hkv))
+    _run_and_compare(q, k, v, q_idx, kv_ptr, kv_idx, causal, "head quads", kv_share=4)
+
+
+@pytest.mark.parametrize("pattern", ["scatter", "gather1"])
+def test_head_quads_intra(pattern):
+    B, Hq, Hkv, N = 1, 8, 2, 4096 + 40
+    q, k, v = _qkv(90 + len(pattern), B, Hq, Hkv, N)
+    f = synth.cqs_scatter if pattern == "scatter" else synth.cqs_gather1
+    maps = synth.cqs_per_head(f(N, 8, 64, True), B * Hq)
+    _log("case tok head quads INTRA %s N=%d" % (pattern, N))
+    _run_and_compare(q, k, v, *maps, True, pattern + " head quads", kv_share=4)
 
 
 @pytest.mark.parametrize("pattern", ["scatter", "gather1"])
