@@ -386,9 +386,15 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
     l_tot = l_w * a1 + l2 * a2;
   }
-  if (!qok) return;
+  // Normalised rows of this wavefront's 32 queries: staged in LDS as bf16
+  // rows of 256 bytes (chunk c of row r at chunk position c ^ (r mod 16)),
+  // then written out as whole rows, 16 lanes per row, instead of 16-byte
+  // pieces of 32 rows per store (far fewer, full-line writes to drain
+  // before the workgroup ends).  The stage buffers are free: with key
+  // halves the merge used k0 and v0, and k1 takes the rows; otherwise every
+  // wavefront is past the last tile.
+  uint8_t *const obuf = KSPLIT == 2 ? k1 + gi * 8192 : &stg[0][0] + wave * 8192;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t *ob16 = p.o + b * p.os0 + h * p.os1 + (int64_t)qi * p.os2;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -401,10 +407,19 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] *= inv;
-      *reinterpret_cast<uint2 *>(ob16 + 32 * dt + 8 * i4 + 4 * hf) =
+      // dims 32 dt + 8 i4 + 4 hf .. +3: half hf of chunk 4 dt + i4 of row ln
+      *reinterpret_cast<uint2 *>(obuf + ln * 256 + (((4 * dt + i4) ^ (ln & 15)) << 4) + 8 * hf) =
           make_uint2(cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3]));
     }
-  if (p.lse && hf == 0) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
+  uint16_t *const obase = p.o + b * p.os0 + h * p.os1;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int row = 4 * t + (lane >> 4), ch = lane & 15;
+    const int qr = __shfl(qi, row);   // lane `row` (hf = 0) holds that row's query
+    const uint4 val = *reinterpret_cast<const uint4 *>(obuf + row * 256 + ((ch ^ (row & 15)) << 4));
+    if (qr >= 0) *reinterpret_cast<uint4 *>(obase + (int64_t)qr * p.os2 + 8 * ch) = val;
+  }
+  if (p.lse && hf == 0 && qok) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // 64-query sets: 4 wavefronts (two query groups x key halves), two per CU;
