@@ -55,6 +55,10 @@ def parse():
                          "print them as one JSON line, and exit")
     ap.add_argument("--token-sets-only", action="store_true",
                     help="instead of the step: run only the token-level set measurements and print them")
+    ap.add_argument("--kv-share-ab", action="store_true",
+                    help="instead of the step: time the LLaMA-3.1-8B prefill workload's attention alone with "
+                         "the per-head kernel and with the query-head-pair kernel (alternating, median of 20 "
+                         "each), compare their outputs, print one JSON line and exit")
     ap.add_argument("--n-xcd", type=int, default=8)
     ap.add_argument("--wave-rows", type=int, default=0)
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -126,6 +130,9 @@ def main():
         return
     if args.token_sets_only:
         print(json.dumps({"token_sets": token_set_stage(torch)}), flush=True)
+        return
+    if args.kv_share_ab:
+        print(json.dumps({"kv_share_ab": kv_share_ab(args, torch)}), flush=True)
         return
 
     t0 = time.time()
@@ -425,6 +432,61 @@ def sampler_stage(dw, torch, m_exact=8, m_sample=8):
                 "attention_ms": round(att, 4),
                 "attention_tflops": round(4.0 * dw.d * pairs / (att * 1e-3) / 1e12, 2)})
     return out
+
+
+def kv_share_ab(args, torch):
+    """The LLaMA-3.1-8B prefill workload's attention alone, per-head kernel
+    (one row per workgroup) against the query-head-pair kernel (one
+    workgroup per pair of identical rows of query heads 2j, 2j + 1): both
+    launched on the same inputs, alternating, 10 warm-up calls and 20 timed
+    launches each; the two outputs are compared (the same function up to
+    rounding order)."""
+    from block_sparse_attention_mask_amd import api, metrics, pipeline
+    import synth
+    w = synth.CONFIGS["llm_prefill"]()
+    dw = pipeline.to_device(w, torch.device("cuda"))
+    row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
+    if not kv_share_ok(dw, row_ptr, col, lw):
+        raise SystemExit("the prefill rows are not pair-identical")
+    v = api.transpose_rows(dw.v, None, ld=dw.nQB * dw.block)
+    outs, launches = {}, {}
+    for share in (False, True):
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                             head_step=2 if share else 1, col=col)
+        out = torch.empty((dw.B, dw.Hq, dw.N, dw.d), dtype=dw.q.dtype, device=dw.q.device)
+        outs[share] = out
+        launches[share] = (lambda o=order, out=out, share=share: api.attn_fwd(
+            dw.q, dw.k, v, row_ptr, col, dw.block, lw=lw, order=o, causal=dw.causal, v_dim_major=True,
+            out=out, kv_share=share))
+    s = torch.cuda.current_stream()
+    for _ in range(10):
+        for share in (False, True):
+            launches[share]()
+    ms = {False: [], True: []}
+    for _ in range(20):
+        for share in (False, True):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            launches[share]()
+            b.record(s)
+            torch.cuda.synchronize()
+            ms[share].append(a.elapsed_time(b))
+    rp = row_ptr.cpu().numpy()
+    nnz = int(rp[-1])
+    pairs = metrics.count_pairs(rp, col[:nnz].cpu().numpy(), w.N, w.block, w.causal)
+    flop = 4.0 * w.d * pairs
+    as_f32 = lambda t: (t.view(torch.bfloat16) if t.dtype in (torch.int16, torch.uint16) else t).float()
+    diff = (as_f32(outs[False]) - as_f32(outs[True])).abs()
+    res = {"workload": workload_name("llm_prefill"), "effective_gflop": round(flop / 1e9, 3),
+           "max_abs_diff": float(diff.max().item()), "mean_abs_diff": float(diff.mean().item())}
+    for share, key in ((False, "per_head"), (True, "head_pairs")):
+        t = float(np.median(ms[share]))
+        res[key] = {"kernel": attn_kernel_name(w.block, w.d, share), "median_ms": round(t, 4),
+                    "tflops": round(flop / (t * 1e-3) / 1e12, 2),
+                    "frac": round(flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log("kv_share A/B: per head %.3f ms, head pairs %.3f ms" % (res["per_head"]["median_ms"],
+                                                                res["head_pairs"]["median_ms"]))
+    return res
 
 
 def token_set_stage(torch):
