@@ -10,19 +10,26 @@
 // sequence and, when causal, keys s_e > t do not take part.  Outputs go back
 // to the query positions (INTRA, section 4.8).
 //
-// Mapping to the hardware (one workgroup per set, or per pair of sets of
-// the two query heads 2j, 2j + 1 of a KV group when their query slots and
+// Mapping to the hardware (one workgroup per set, or per run of the sets of
+// 2 or 4 consecutive query heads of a KV group when their query slots and
 // key lists are identical; BQ = 64 or 128 queries, head dim 128, 64-key
-// tiles; four wavefronts, two workgroups per CU):
+// tiles; four wavefronts and two workgroups per CU, or eight wavefronts and
+// one workgroup per CU for runs of four heads):
 //   * 64-query sets of one head: wavefront w owns the 32 queries of group
 //     w % 2 and the key half w / 2 (keys 0-31 or 32-63 of every tile), with
 //     its own online-softmax state; the halves merge once through LDS at the
 //     end.
-//   * 128-query sets, and pairs of 64-query sets: wavefront w owns 32
-//     queries (query group, or head and query group) and every key of every
-//     tile (two 32-key M tiles per step), so no merge is needed.  With two
-//     heads every gathered tile serves both, halving the gather traffic per
-//     unit of work.
+//   * 128-query sets, and runs of 64-query sets: wavefront w owns 32 queries
+//     (query group, or head and query group) and every key of every tile
+//     (two 32-key M tiles per step), so no merge is needed.  With 2 or 4
+//     heads every gathered tile serves all of them, dividing the gather
+//     traffic per unit of work by 2 or 4.
+//   * The sets are dealt to the XCDs in contiguous shares, so that an XCD
+//     runs neighbouring sets, which list mostly the same keys, at the same
+//     time and its L2 holds their K and V rows.
+//   * The first chunk of a set's list is loaded into registers together with
+//     its query slots; the normalised outputs are staged in LDS and written
+//     as whole 256-byte rows.
 //   * The selected K and V rows are gathered straight into LDS by
 //     buffer_load_dwordx4 ... lds: each lane copies one 16-byte chunk of one
 //     key row, with the row's position taken from the staged key list, so a
@@ -424,7 +431,7 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
 
 // 64-query sets: 4 wavefronts (two query groups x key halves), two per CU;
 // 128-query sets and pairs of 64-query sets: 4 wavefronts that each take
-// whole tiles, two per CU
+// whole tiles, two per CU; runs of four 64-query sets: 8 wavefronts, one per CU
 #define BSA_TOK_KERNEL(NAME, BQ, HP, KSPLIT)                                                        \
   __global__ __attribute__((amdgpu_flat_work_group_size(TCfg<BQ, HP, KSPLIT>::NT, TCfg<BQ, HP, KSPLIT>::NT), \
                             amdgpu_waves_per_eu(2, 2)))                                             \
