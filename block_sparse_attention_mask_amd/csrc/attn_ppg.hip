@@ -398,20 +398,35 @@ __device__ __forceinline__ void attn_ppg_body(const AttnParams &p, const int32_t
     // normalise and store this wavefront's queries
     const float l_tot = halves_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int oi = (qi < N && sperm) ? sperm[bh * N + qi] : qi;
-    if (qi < N && oi >= 0 && oi < N) {
-      uint16_t *ob16 = out + b * p.os0 + h * p.os1 + (int64_t)oi * p.os2;
+    int oi = (qi < N && sperm) ? sperm[bh * N + qi] : qi;
+    if (!(qi < N && oi >= 0 && oi < N)) oi = -1;   // padding query, or a scatter entry outside the rows
+    // The rows are staged in this wavefront's 32 D bytes of the stage buffers
+    // (every wavefront has passed the barrier after the last phase) as bf16
+    // rows, chunk c of row r at chunk position c ^ (r mod KC), then written
+    // out as whole rows, 64 / KC rows per store, instead of 16-byte pieces of
+    // 32 rows (fewer, full-line writes to drain before the workgroup ends).
+    static_assert(C::NW * 32 * 2 * D <= 6 * C::KB, "every wavefront's rows fit the stage buffers");
+    uint8_t *const obuf = smem + wave * (32 * 2 * D);
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float x0 = o[dt][4 * i4] * inv, x1 = o[dt][4 * i4 + 1] * inv;
-          const float x2 = o[dt][4 * i4 + 2] * inv, x3 = o[dt][4 * i4 + 3] * inv;
-          *reinterpret_cast<uint2 *>(ob16 + 32 * dt + 8 * i4 + 4 * hf) =
-              make_uint2(cvt_pk_bf16(x0, x1), cvt_pk_bf16(x2, x3));
-        }
-      if (lse && hf == 0) lse[bh * N + oi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float x0 = o[dt][4 * i4] * inv, x1 = o[dt][4 * i4 + 1] * inv;
+        const float x2 = o[dt][4 * i4 + 2] * inv, x3 = o[dt][4 * i4 + 3] * inv;
+        // dims 32 dt + 8 i4 + 4 hf .. +3: half hf of chunk 4 dt + i4 of row ln
+        *reinterpret_cast<uint2 *>(obuf + ln * (2 * D) + (((4 * dt + i4) ^ (ln % C::KC)) << 4) + 8 * hf) =
+            make_uint2(cvt_pk_bf16(x0, x1), cvt_pk_bf16(x2, x3));
+      }
+    uint16_t *const ob16 = out + b * p.os0 + h * p.os1;
+    constexpr int RPS = 64 / C::KC;   // rows per store
+#pragma unroll
+    for (int t = 0; t < 32 / RPS; ++t) {
+      const int row = RPS * t + lane / C::KC, ch = lane % C::KC;
+      const int orow = __shfl(oi, row);   // lane `row` (hf = 0) holds that row's destination
+      const uint4 val = *reinterpret_cast<const uint4 *>(obuf + row * (2 * D) + ((ch ^ (row % C::KC)) << 4));
+      if (orow >= 0) *reinterpret_cast<uint4 *>(ob16 + (int64_t)orow * p.os2 + 8 * ch) = val;
     }
+    if (lse && hf == 0 && oi >= 0) lse[bh * N + oi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   };
   if (hd == 0) run(std::integral_constant<int, 0>());
   else run(std::integral_constant<int, 1>());
