@@ -856,6 +856,21 @@ def rows_pairs(w, rp, col, rows, perm_q):
     return out
 
 
+def host_cpu():
+    """The host's CPU model (first "model name" of /proc/cpuinfo) and the
+    number of CPUs the OS reports, for the CPU baseline's record."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def oracle_leg(w, gpu_out, gpu_lse, gpu_csr, torch, seed=1234):
     """The CPU reference checker (fp64, every host thread) on the measurement
     protocol's row set: its own CSR and permutations from the workload's
@@ -890,6 +905,7 @@ def oracle_leg(w, gpu_out, gpu_lse, gpu_csr, torch, seed=1234):
            "seconds": round(dt, 3), "rows": int(len(rows)), "rows_per_s": round(len(rows) / dt, 1),
            "extrapolated_full_seconds": round(dt * w.B * w.Hq * w.N / len(rows), 1),
            "oracle_csr_and_perm_seconds": round(t_prep, 3),
+           "host": host_cpu(),
            "csr_bit_exact": csr_exact,
            "max_abs": float(err.max()), "mean_abs": float(err.mean())}
     if gpu_lse is not None:
