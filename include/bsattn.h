@@ -385,11 +385,14 @@ int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t B, int32_t 
  * writes; per-head byte extents of q, k and v must stay below 2^30) or
  * BSA_V_TOKEN_MAJOR.  o must not alias q, k or v.  lse (float32 [B*Hq][N],
  * contiguous, device, optional) receives ln(sum_j exp(l_ij + log w_j)) of
- * every query.  row_ptr/col/lw: CSR as built above (lw optional).  order
+ * every query.  row_ptr/col/lw: CSR as built above (lw optional); a block
+ * index outside [0, nQB) in col takes no part (its keys are masked).  order
  * (optional, int32 [R]): launch index -> row; rows not listed are not
- * computed.  scatter_perm_q (optional, int32 [B*Hq][N]): when set, the output
- * of the query at position i is written to position scatter_perm_q[bh][i] of
- * o (and lse), i.e. the inverse permutation is fused into the store.
+ * computed, nor is anything for an entry outside [0, R).  scatter_perm_q
+ * (optional, int32 [B*Hq][N]): when set, the output of the query at position
+ * i is written to position scatter_perm_q[bh][i] of o (and lse), i.e. the
+ * inverse permutation is fused into the store; an entry outside [0, N) writes
+ * nothing.
  * gather_perm_q (optional, int32 [B*Hq][N]): when set, q is unpermuted and
  * the query at permuted position i is row gather_perm_q[bh][i] of q (the
  * query gather fused into the load; an entry outside [0, N) reads zeros).
