@@ -228,6 +228,7 @@ def main():
             others[cfg] = workload_line(cfg, args, torch, with_oracle=not args.no_cpu_baseline)
             torch.cuda.empty_cache()
 
+    dev = device_info(torch)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -257,7 +258,7 @@ def main():
                         "alone_median50_ms": attn_solo["median_ms"],
                         "alone_median50_tflops": round(eff_flops / (attn_solo["median_ms"] * 1e-3) / 1e12, 2),
                         "l2_flushed_ms": attn_solo["flushed_ms"]},
-        "device": device_info(torch),
+        "device": dev,
         "stages_ms": stages,
         "stage1_adaptive_skip": stage1,
         "crm_lists": crm,
@@ -268,6 +269,8 @@ def main():
                           "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4)},
                          **profile_record(args.config),
                          **{"traffic_unit": "HBM-side bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                            "frac_of_mfma_rate_random_bf16": round(
+                                attn_tflops / dev["mfma_random_bf16_operands"]["tflops"], 4),
                             "kernel": attn_kernel_name(w.block, w.d),
                             "per_unit": "4*d = 512 FLOP per allowed query-key pair",
                             "units_per_launch": pairs}),
@@ -649,9 +652,16 @@ def selection_stage(torch):
 def device_info(torch):
     from block_sparse_attention_mask_amd import api
     p = torch.cuda.get_device_properties(0)
+    # the matrix cores with constant operands, then with random bf16 operands
+    # (every MFMA sees new bits, as on the workloads' inputs): the engine
+    # clock, and so the rate, falls with the operand bits that switch.  A
+    # short call of each kind first, so that neither reads a cold start.
+    api.clock_under_mfma_load(iters=4000)
+    api.clock_under_mfma_load(iters=4000, random_operands=True)
     return {"name": p.name, "arch": p.gcnArchName, "cus": api.device_cus(),
             "peak_sclk_mhz": api.device_clock_khz() // 1000,
-            "sclk_mhz_under_mfma_load": api.clock_under_mfma_load()}
+            "sclk_mhz_under_mfma_load": api.clock_under_mfma_load(),
+            "mfma_random_bf16_operands": api.clock_under_mfma_load(random_operands=True)}
 
 
 def profile_record(cfg):

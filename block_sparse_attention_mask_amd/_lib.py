@@ -141,7 +141,7 @@ def load():
         L.bsa_attn_fwd.restype = ctypes.c_int
         L.bsa_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), P]
         L.bsa_clock_probe.restype = ctypes.c_int
-        L.bsa_clock_probe.argtypes = [I32, I32, P, P]
+        L.bsa_clock_probe.argtypes = [I32, I32, I32, P, P]
         L.bsa_attn_tok_fwd.restype = ctypes.c_int
         L.bsa_attn_tok_fwd.argtypes = [ctypes.POINTER(TokArgs), P]
         L.bsa_group_mass.restype = ctypes.c_int

@@ -65,17 +65,28 @@ def device_clock_khz() -> int:
     return k
 
 
-def clock_under_mfma_load(blocks: int = 0, iters: int = 20000, stream=None) -> dict:
-    """bsa_clock_probe over every CU (4 workgroups per CU by default):
-    median, min and max engine clock in MHz of the wavefronts."""
+def clock_under_mfma_load(blocks: int = 0, iters: int = 40000, random_operands: bool = False,
+                          stream=None) -> dict:
+    """bsa_clock_probe over every CU (2 workgroups per CU by default, so that
+    every wavefront is resident from start to end):
+    median, min and max engine clock in MHz of the wavefronts, and the MFMA
+    rate of the launch in TFLOP/s (HIP events around it on its stream).  With
+    ``random_operands`` every MFMA sees new random bf16 operands."""
     if blocks <= 0:
-        blocks = 4 * device_cus()
+        blocks = 2 * device_cus()
     ticks = torch.zeros(4 * blocks * 2, dtype=torch.int64, device="cuda")
-    check("bsa_clock_probe", load().bsa_clock_probe(int(blocks), int(iters), _ptr(ticks), _stream(stream)))
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    check("bsa_clock_probe", load().bsa_clock_probe(int(blocks), int(iters), int(bool(random_operands)),
+                                                    _ptr(ticks), _stream(s)))
+    e1.record(s)
     torch.cuda.synchronize()
     t = ticks.cpu().numpy().reshape(-1, 2).astype("float64")
     mhz = sorted(t[:, 0] / t[:, 1] * 100.0)
-    return {"median": round(mhz[len(mhz) // 2], 1), "min": round(mhz[0], 1), "max": round(mhz[-1], 1)}
+    flop = 4.0 * iters * 32768.0 * 4 * blocks
+    return {"median": round(mhz[len(mhz) // 2], 1), "min": round(mhz[0], 1), "max": round(mhz[-1], 1),
+            "tflops": round(flop / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)}
 
 
 def csr_count(mask=None, T=None, p: float = 0.0, nQB: Optional[int] = None, force_diag: bool = True,

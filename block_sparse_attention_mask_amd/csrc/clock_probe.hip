@@ -2,6 +2,10 @@
 // independent v_mfma_f32_32x32x16_bf16 chains and records how far the shader
 // clock counter (s_memtime) and the constant 100 MHz counter (s_memrealtime)
 // advanced; their ratio times 100 MHz is the clock the wavefront ran at.
+// The operands are either constant and low in entropy, or random bf16
+// values that change on every MFMA: the engine clock under MFMA load depends
+// on how many operand bits switch, so the second form gives the clock and the
+// rate the matrix cores sustain on data like the attention inputs.
 #include "bsa_internal.h"
 
 namespace {
@@ -9,20 +13,54 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// 32-bit integer hash (xorshift-multiply rounds) for the random operands
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// uniform in [-2, 2) from the hash's low 24 bits
+__device__ __forceinline__ __bf16 uniform_bf16(uint32_t h) {
+  return (__bf16)((float)(h & 0xffffffu) * (4.0f / 16777216.0f) - 2.0f);
+}
+
+template <bool RANDOM>
 __global__ __launch_bounds__(256) void clock_probe_kernel(int iters, uint64_t *__restrict__ ticks) {
-  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  bf16x8 a, b;
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)((threadIdx.x & 7) * 0.001f);
-    b[i] = (__bf16)(i * 0.001f);
-  }
+  // eight A and eight B operands per lane; the constant form repeats one of each
+  bf16x8 a[8], b[8];
+  const uint32_t lane_id = (uint32_t)(blockIdx.x * 256 + threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (RANDOM) {
+        a[j][i] = uniform_bf16(mix32(lane_id * 131u + 16u * j + i));
+        b[j][i] = uniform_bf16(mix32(lane_id * 131u + 16u * j + i + 0x9e3779b9u));
+      } else {
+        a[j][i] = (__bf16)((threadIdx.x & 7) * 0.001f);
+        b[j][i] = (__bf16)(i * 0.001f);
+      }
+    }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
-  for (int it = 0; it < iters; ++it) {
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
-    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  // one iteration is four MFMAs (one per chain); two iterations use all
+  // eight operand pairs
+  auto mfma_round = [&](int j) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(j + 1) & 7], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j + 1], b[(j + 2) & 7], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j + 2], b[(j + 3) & 7], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j + 3], b[(j + 4) & 7], c3, 0, 0, 0);
+  };
+  int it = 0;
+  for (; it + 1 < iters; it += 2) {
+    mfma_round(0);
+    mfma_round(4);
   }
+  if (it < iters) mfma_round(0);
   const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
@@ -35,9 +73,15 @@ __global__ __launch_bounds__(256) void clock_probe_kernel(int iters, uint64_t *_
 
 }  // namespace
 
-extern "C" int bsa_clock_probe(int32_t blocks, int32_t iters, uint64_t *ticks, bsa_stream_t stream) {
+extern "C" int bsa_clock_probe(int32_t blocks, int32_t iters, int32_t random_operands, uint64_t *ticks,
+                               bsa_stream_t stream) {
   if (!ticks || blocks <= 0 || iters <= 0) return BSA_ERR_ARG;
-  hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, bsa_hip_stream(stream), iters, ticks);
+  if (random_operands)
+    hipLaunchKernelGGL(clock_probe_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, bsa_hip_stream(stream), iters,
+                       ticks);
+  else
+    hipLaunchKernelGGL(clock_probe_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, bsa_hip_stream(stream), iters,
+                       ticks);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

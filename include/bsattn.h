@@ -573,13 +573,18 @@ int bsa_topk_rows(const float *x, int64_t rows, int64_t n, int64_t ld, int32_t k
  * Engine-clock probe under MFMA load (for reading a measurement against the
  * clock the device sustains, not the path itself).  Launches `blocks`
  * workgroups of four wavefronts; each wavefront runs `iters` iterations of
- * four independent 32x32x16 bf16 MFMA chains and writes, at ticks[2w] and
- * ticks[2w + 1] (device uint64 [4 * blocks][2], caller-owned), how far the
- * shader clock counter and the 100 MHz real-time counter advanced; the
- * wavefront's clock is ticks[2w] / ticks[2w + 1] * 100 MHz.  BSA_ERR_ARG for
- * NULL or non-positive sizes.  Asynchronous.
+ * four independent 32x32x16 bf16 MFMA chains (4 * iters * 32768 FLOP) and
+ * writes, at ticks[2w] and ticks[2w + 1] (device uint64 [4 * blocks][2],
+ * caller-owned), how far the shader clock counter and the 100 MHz real-time
+ * counter advanced; the wavefront's clock is ticks[2w] / ticks[2w + 1] *
+ * 100 MHz.  random_operands = 0: constant, low-entropy operands;
+ * random_operands != 0: each lane cycles through eight A and eight B operands
+ * of bf16 values drawn uniformly from [-2, 2), so every MFMA sees new random
+ * bits (the clock under MFMA load falls as more operand bits switch).
+ * BSA_ERR_ARG for NULL or non-positive sizes.  Asynchronous.
  * ------------------------------------------------------------------------- */
-int bsa_clock_probe(int32_t blocks, int32_t iters, uint64_t *ticks, bsa_stream_t stream);
+int bsa_clock_probe(int32_t blocks, int32_t iters, int32_t random_operands, uint64_t *ticks,
+                    bsa_stream_t stream);
 
 /* Number of compute units of the current device (for wave sizing), or a
  * negative error. */

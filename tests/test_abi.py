@@ -112,9 +112,9 @@ def test_spectral_order_argument_errors(L):
 
 
 def test_clock_probe_argument_errors(L):
-    assert L.bsa_clock_probe(4, 100, None, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_clock_probe(0, 100, FAKE, None) == _lib.BSA_ERR_ARG
-    assert L.bsa_clock_probe(4, 0, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_clock_probe(4, 100, 0, None, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_clock_probe(0, 100, 1, FAKE, None) == _lib.BSA_ERR_ARG
+    assert L.bsa_clock_probe(4, 0, 0, FAKE, None) == _lib.BSA_ERR_ARG
 
 
 def test_crm_argument_errors(L):
