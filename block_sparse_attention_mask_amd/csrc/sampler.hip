@@ -10,16 +10,17 @@
 // Sampler: one workgroup per (head, query group).  The tile is the unit of
 // Algorithm 1 at tile granularity: its centroid is its mean key and its
 // size its number of real keys.  The workgroup computes the tile masses
-// |v| exp(scale q_g . k_v - max) in fp64, ranks them (count of larger
-// masses, ties to the lower tile), takes the m_exact largest as the exact
-// set, water-fills the inclusion probabilities of the rest (Eq. 4: the
-// number k of capped tiles is the smallest k for which the k-th largest
-// residual mass is not capped by lam = (m - k) / (sum of the masses from
-// the k-th on)), draws the systematic PPS sample (points u0 + j of the
-// running sum of pi over the residual in ascending tile order), and writes
-// the mask and log-weight rows (-ln pi for a sampled tile with pi < 1, else
-// 0; 0 on the diagonal) of every query block of the group.  Sums over tiles
-// are fixed-order scans, so the result does not depend on timing.
+// |v| exp(scale q_g . k_v - max) in fp64, finds the m_exact + m_sample
+// largest in (mass descending, tile ascending) order (the only ranks the
+// rest needs), takes the m_exact largest as the exact set, water-fills the
+// inclusion probabilities of the rest (Eq. 4: the number k of capped tiles
+// is the smallest k for which the k-th largest residual mass is not capped
+// by lam = (m - k) / (sum of the masses from the k-th on)), draws the
+// systematic PPS sample (points u0 + j of the running sum of pi over the
+// residual in ascending tile order), and writes the mask and log-weight rows
+// (-ln pi for a sampled tile with pi < 1, else 0; 0 on the diagonal) of every
+// query block of the group.  Sums over tiles are fixed-order reductions and
+// scans, so the result does not depend on timing.
 #include <math.h>
 
 #include "bsa_internal.h"
@@ -136,15 +137,15 @@ __device__ double block_max(double v, double *red) {
   return r;
 }
 
-__device__ int block_min_int(int v, int *red) {
+__device__ double block_sum(double v, double *red) {
   const int t = threadIdx.x;
   red[t] = v;
   __syncthreads();
   for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (t < s) red[t] = min(red[t], red[t + s]);
+    if (t < s) red[t] += red[t + s];
     __syncthreads();
   }
-  const int r = red[0];
+  const double r = red[0];
   __syncthreads();
   return r;
 }
@@ -173,18 +174,27 @@ __device__ void block_scan(double *a, int n, double *tot) {
   __syncthreads();
 }
 
+// Ranks up to this many are found by rounds of a workgroup-wide argmax;
+// larger selections count, for every tile, the tiles before it.
+constexpr int kTopFast = 64;
+
 __global__ __launch_bounds__(kThreads) void is_sample_kernel(
     const float *__restrict__ qbar, const float *__restrict__ kbar, const int32_t *__restrict__ q_seg_ptr,
     const double *__restrict__ uoff, int Hq, int Hkv, int G, int64_t N, int block, int d, int m_exact,
     int m_sample, double scale, uint8_t *__restrict__ mask, float *__restrict__ lw_map,
     double *__restrict__ pi_out) {
-  __shared__ double mass[kMaxTiles], pi[kMaxTiles], sres[kMaxTiles], cum[kMaxTiles];
-  __shared__ int32_t rnk[kMaxTiles];
+  // per tile: its mass; the running sum of pi in tile order (before that, the
+  // residual's suffix sums); its rank in (mass descending, tile ascending)
+  // order where that is below K, else K
+  __shared__ double mass[kMaxTiles], cum[kMaxTiles];
+  __shared__ int32_t rk[kMaxTiles];
+  __shared__ int32_t top[kMaxTiles];   // top[j]: the tile of rank j, j < K
   __shared__ float lwv[kMaxTiles];
   __shared__ uint8_t keep[kMaxTiles];
   __shared__ float qs[kMaxD];
   __shared__ double red[kThreads];
-  __shared__ int ired[kThreads];
+  __shared__ double lam_s;
+  __shared__ int k_s;
   const int t = threadIdx.x;
   const int g = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -207,66 +217,170 @@ __global__ __launch_bounds__(kThreads) void is_sample_kernel(
     for (int v = t; v < nb; v += kThreads) pi_out[(bh * G + g) * nb + v] = 0.0;
   if (u0 >= u1) return;
 
-  // step 2: centroid scores and tile masses
+  // step 2: centroid scores and tile masses.  A thread's tiles are
+  // v = t + kThreads i; their dot products run as independent chains (each
+  // in order over the dims), tiles past the last reading the last one's row.
   for (int c = t; c < d; c += kThreads) qs[c] = qbar[(bh * G + g) * d + c];
   __syncthreads();
+  constexpr int kPerT = kMaxTiles / kThreads;
+  double dot[kPerT];
+  const float *kv[kPerT];
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) {
+    const int v = t + kThreads * i;
+    kv[i] = kbar + (gk * nb + (v < nb ? v : nb - 1)) * d;
+    dot[i] = 0.0;
+  }
+  for (int c = 0; c < d; ++c) {
+    const double qc = (double)qs[c];
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) dot[i] += qc * (double)kv[i][c];
+  }
   double amax = -INFINITY;
-  for (int v = t; v < nb; v += kThreads) {
-    const float *kv = kbar + (gk * nb + v) * d;
-    double s = 0.0;
-    for (int c = 0; c < d; ++c) s += (double)qs[c] * (double)kv[c];
-    mass[v] = scale * s;
-    amax = fmax(amax, mass[v]);
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) {
+    const int v = t + kThreads * i;
+    if (v < nb) {
+      mass[v] = scale * dot[i];
+      amax = fmax(amax, mass[v]);
+    }
   }
   amax = block_max(amax, red);
+  const int ne = m_exact < nb ? m_exact : nb;
+  const int nr = nb - ne;
+  const bool capped = nr > m_sample;              // the residual needs water-filling
+  const int K = capped ? ne + m_sample : ne;      // ranks needed: the exact set and the residual's largest
   for (int v = t; v < nb; v += kThreads) {
     const int64_t size = N - (int64_t)v * block < block ? N - (int64_t)v * block : block;
     mass[v] = (double)size * exp(mass[v] - amax);
+    rk[v] = K;
   }
+  for (int j = t; j < K; j += kThreads) top[j] = 0;
   __syncthreads();
-  // step 4: rank by (mass descending, tile ascending); the exact set is the
-  // first m_exact
-  for (int v = t; v < nb; v += kThreads) {
-    const double m = mass[v];
-    int r = 0;
-    for (int w = 0; w < nb; ++w) {
-      const double x = mass[w];
-      r += (x > m) || (x == m && w < v);
+
+  // step 4: the K first tiles in (mass descending, tile ascending) order;
+  // the exact set is the first m_exact.  For K <= kTopFast every wavefront
+  // takes its own K first tiles by K rounds of a wavefront argmax over its
+  // lanes' tiles (registers and shuffles only); every tile among the K first
+  // overall is among its wavefront's K first, so counting within the union
+  // of the wavefronts' lists gives those tiles their rank, and every other
+  // candidate a count of at least K.
+  if (K <= kTopFast) {
+    double* const cm = cum;                                  // candidates' masses (cum is free here)
+    int32_t* const cv = reinterpret_cast<int32_t *>(lwv);   // and tiles (lwv is free here)
+    const int lane = t & 63, wave = t >> 6;
+    double m[kPerT];
+    bool avail[kPerT];
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int v = t + kThreads * i;
+      avail[i] = v < nb;
+      m[i] = avail[i] ? mass[v] : 0.0;
     }
-    rnk[v] = r;
-  }
-  __syncthreads();
-  const int ne = m_exact < nb ? m_exact : nb;
-  const int nr = nb - ne;
-  // step 10: inclusion probabilities of the residual
-  if (nr <= m_sample) {
-    for (int v = t; v < nb; v += kThreads) pi[v] = 1.0;
-  } else {
-    // residual masses in ascending order (cum), and their running sums from
-    // the smallest up (sres): the i-th largest (i from 0) is cum[nr-1-i], and
-    // it plus every smaller one sums to sres[nr-1-i]
-    for (int v = t; v < nb; v += kThreads)
-      if (rnk[v] >= ne) cum[nb - 1 - rnk[v]] = sres[nb - 1 - rnk[v]] = mass[v];
+    for (int j = 0; j < K; ++j) {
+      double bm = -1.0;   // masses are >= 0
+      int bv = nb;
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int v = t + kThreads * i;
+        if (avail[i] && (m[i] > bm || (m[i] == bm && v < bv))) {
+          bm = m[i];
+          bv = v;
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const double om = __shfl_xor(bm, off);
+        const int ov = __shfl_xor(bv, off);
+        if (om > bm || (om == bm && ov < bv)) {
+          bm = om;
+          bv = ov;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i)
+        if (t + kThreads * i == bv) avail[i] = false;
+      if (lane == 0) {
+        cm[wave * K + j] = bm;
+        cv[wave * K + j] = bv;
+      }
+    }
     __syncthreads();
-    block_scan(sres, nr, red);
-    int kk = m_sample;
-    for (int i = t; i < m_sample; i += kThreads)
-      if ((double)(m_sample - i) * cum[nr - 1 - i] <= sres[nr - 1 - i]) kk = min(kk, i);
-    const int k = block_min_int(kk, ired);
-    const double lam = (double)(m_sample - k) / sres[nr - 1 - k];
-    for (int v = t; v < nb; v += kThreads) {
-      const int i = rnk[v] - ne;
-      pi[v] = i < 0 ? 1.0 : (i < k ? 1.0 : lam * mass[v]);
+    const int nc = (kThreads / 64) * K;
+    for (int c = t; c < nc; c += kThreads) {
+      const double mc = cm[c];
+      const int vc = cv[c];
+      if (vc >= nb) continue;   // a wavefront with fewer than K tiles
+      int r = 0;
+      for (int e = 0; e < nc; ++e) {
+        const int ve = cv[e];
+        const double me = cm[e];
+        r += ve < nb && (me > mc || (me == mc && ve < vc));
+      }
+      if (r < K) {
+        rk[vc] = r;
+        top[r] = vc;
+      }
     }
+    __syncthreads();
+  } else {
+    for (int v = t; v < nb; v += kThreads) {
+      const double m = mass[v];
+      int r = 0;
+      for (int w = 0; w < nb; ++w) {
+        const double x = mass[w];
+        r += (x > m) || (x == m && w < v);
+      }
+      if (r < K) {
+        rk[v] = r;
+        top[r] = v;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
+
+  // step 10: inclusion probabilities of the residual.  With r_i the i-th
+  // largest residual mass (rank ne + i) and S_i the sum of r_i and every
+  // smaller one, k is the first i < m_sample with (m_sample - i) r_i <= S_i
+  // (m_sample if none), lambda = (m_sample - k) / S_k; the residual's k
+  // largest get pi = 1 and the rest lambda * mass.  S_i is the sum of the
+  // tiles past rank K plus r_{m_sample-1} ... r_i.
+  int k = 0;
+  double lam = 0.0;
+  if (capped) {
+    double tail = 0.0;
+    for (int v = t; v < nb; v += kThreads)
+      if (rk[v] >= K) tail += mass[v];
+    tail = block_sum(tail, red);
+    if (t == 0) {
+      double S = tail;
+      cum[m_sample] = S;
+      for (int i = m_sample - 1; i >= 0; --i) {
+        S += mass[top[ne + i]];
+        cum[i] = S;
+      }
+      int kk = m_sample;
+      for (int i = 0; i < m_sample; ++i)
+        if ((double)(m_sample - i) * mass[top[ne + i]] <= cum[i]) {
+          kk = i;
+          break;
+        }
+      k_s = kk;
+      lam_s = (double)(m_sample - kk) / cum[kk];
+    }
+    __syncthreads();
+    k = k_s;
+    lam = lam_s;
+  }
+  auto pi_of = [&](int v) -> double { return (!capped || rk[v] < ne + k) ? 1.0 : lam * mass[v]; };
+
   // step 11: systematic PPS over the residual in ascending tile order
-  for (int v = t; v < nb; v += kThreads) cum[v] = rnk[v] < ne ? 0.0 : pi[v];
+  for (int v = t; v < nb; v += kThreads) cum[v] = rk[v] < ne ? 0.0 : pi_of(v);
   __syncthreads();
   block_scan(cum, nb, red);
   const double uo = uoff[bh * G + g];
   for (int v = t; v < nb; v += kThreads) {
-    const bool ex = rnk[v] < ne;
+    const bool ex = rk[v] < ne;
+    const double pv = pi_of(v);
     bool kept = ex;
     if (!ex) {
       // [lo, hi): the running sum before and after this tile (exact tiles add 0)
@@ -276,8 +390,8 @@ __global__ __launch_bounds__(kThreads) void is_sample_kernel(
     }
     keep[v] = kept ? 1 : 0;
     // step 13: Horvitz-Thompson weight as a log-weight
-    lwv[v] = (kept && !ex && pi[v] < 1.0) ? (float)(-log(pi[v])) : 0.f;
-    if (pi_out) pi_out[(bh * G + g) * nb + v] = pi[v];
+    lwv[v] = (kept && !ex && pv < 1.0) ? (float)(-log(pv)) : 0.f;
+    if (pi_out) pi_out[(bh * G + g) * nb + v] = pv;
   }
   __syncthreads();
   for (int u = u0; u < u1; ++u) {
