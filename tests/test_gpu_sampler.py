@@ -136,6 +136,8 @@ def test_segment_means_match_oracle(d):
     (1, 2, 2, 1000, 128, 32, 3, 5, 9, 1.0),          # residual no larger than the budget
     (1, 1, 1, 64 * 1024, 64, 8, 4, 16, 40, 0.5),     # 1024 tiles
     (1, 2, 2, 3000, 64, 24, 4, 4, 0, 1.0),           # exact set only
+    (1, 2, 1, 20000, 64, 64, 6, 30, 50, 1.5),        # m_exact + m_sample > 64: every tile ranked by count
+    (1, 2, 2, 9000, 64, 32, 5, 64, 0, 1.0),          # 64 exact tiles, the largest budget of the argmax rounds
 ])
 def test_is_sample_matches_oracle(B, Hq, Hkv, N, block, d, G, m_exact, m_sample, spread):
     qbar, kbar, seg, uoff = _problem(N + G, B, Hq, Hkv, N, block, d, G, spread)
