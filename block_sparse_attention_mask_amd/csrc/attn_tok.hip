@@ -12,18 +12,18 @@
 //
 // Mapping to the hardware (one workgroup per set, or per run of the sets of
 // 2 or 4 consecutive query heads of a KV group when their query slots and
-// key lists are identical; BQ = 64 or 128 queries, head dim 128, 64-key
-// tiles; four wavefronts and two workgroups per CU, or eight wavefronts and
-// one workgroup per CU for runs of four heads):
-//   * 64-query sets of one head: wavefront w owns the 32 queries of group
-//     w % 2 and the key half w / 2 (keys 0-31 or 32-63 of every tile), with
-//     its own online-softmax state; the halves merge once through LDS at the
-//     end.
-//   * 128-query sets, and runs of 64-query sets: wavefront w owns 32 queries
-//     (query group, or head and query group) and every key of every tile
-//     (two 32-key M tiles per step), so no merge is needed.  With 2 or 4
-//     heads every gathered tile serves all of them, dividing the gather
-//     traffic per unit of work by 2 or 4.
+// key lists are identical; head dim 128):
+//   * Wavefront w owns 32 queries (query group, or head and query group) and
+//     every key of every tile (one 32-key M tile per 32 keys of the tile), so
+//     no merge is needed.
+//   * 64-query sets of one head: 2 wavefronts over 32-key tiles, the list
+//     staged 1024 entries at a time; 37 KB of LDS, so four sets run on a
+//     CU at once, which hides more of each set's chain of dependent loads
+//     (list, first gathers) than larger tiles would.
+//   * 128-query sets (4 wavefronts) and runs of 2 or 4 heads' 64-query sets
+//     (4 or 8 wavefronts): 64-key tiles, the list staged 2048 entries at a
+//     time, two or one per CU.  With 2 or 4 heads every gathered tile serves
+//     all of them, dividing the gather traffic per unit of work by 2 or 4.
 //   * The sets are dealt to the XCDs in contiguous shares, so that an XCD
 //     runs neighbouring sets, which list mostly the same keys, at the same
 //     time and its L2 holds their K and V rows.
@@ -33,7 +33,7 @@
 //   * The selected K and V rows are gathered straight into LDS by
 //     buffer_load_dwordx4 ... lds: each lane copies one 16-byte chunk of one
 //     key row, with the row's position taken from the staged key list, so a
-//     tile of 64 arbitrary keys lands as two dense [key][dim] tiles.  Rows
+//     tile of arbitrary keys lands as two dense [key][dim] tiles.  Rows
 //     past the list or outside the sequence read as zeros.
 //   * S^T = K Q^T reads K chunks with ds_read_b128 (K rows are stored with
 //     chunk c of row r at chunk position c ^ (r mod 16)).  O^T = V^T P^T needs
@@ -62,26 +62,25 @@ namespace tok {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int BQ, int HP, int KSPLIT>
+template <int BQ, int HP, int BK_, int LIST_>
 struct TCfg {
   static constexpr int D = 128;
   static constexpr int NQG = BQ / 32;             // query groups per head
-  static constexpr int NG = HP * NQG;             // (head, query group) pairs
-  static constexpr int NW = KSPLIT * NG;          // wavefronts: pair x key part
+  static constexpr int NW = HP * NQG;             // wavefronts: one per (head, query group)
   static constexpr int NT = 64 * NW;              // threads
-  static constexpr int BK = 64;                   // keys per tile
-  static constexpr int MTW = 2 / KSPLIT;          // 32-key M tiles of a tile per wavefront
+  static constexpr int BK = BK_;                  // keys per tile
+  static constexpr int MTW = BK / 32;             // 32-key M tiles per tile
   static constexpr int KS = D / 16;               // k-steps of K Q^T
   static constexpr int DT = D / 32;               // 32-dim M tiles of O^T
   static constexpr int TILE = BK * D * 2;         // bytes of a K or V tile
   static constexpr int NCOPY = TILE / 1024;       // 1 KB copies per tile (4 rows each)
   static constexpr int NC = NCOPY / NW;           // copies per wavefront per tile
-  static constexpr int LIST = 2048;               // list entries staged at a time
+  static constexpr int LIST = LIST_;              // list entries staged at a time
   static constexpr int NTL = LIST / BK;           // tiles per staged chunk
-  static_assert(KSPLIT == 1 || KSPLIT == 2, "whole tiles or key halves");
+  static_assert(BK == 32 || BK == 64, "32- or 64-key tiles");
   static_assert(NCOPY % NW == 0, "whole copies per wavefront");
-  static_assert(KSPLIT == 1 || NG <= 4, "merge data of every (head, query group) fits a tile buffer");
-  static_assert(64 * DT * 16 * 4 <= TILE, "merge data of a query group fits a tile buffer");
+  static_assert(LIST % NT == 0 && NTL <= NT, "whole list entries per thread, one flag per thread");
+  static_assert(NW * 8192 <= 4 * TILE, "every wavefront's output rows fit the stage buffers");
 };
 
 struct TokParams {
@@ -97,9 +96,9 @@ struct TokParams {
 
 __device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + 2 * ((r >> 3) & 1); }
 
-template <int BQ, int HP, int KSPLIT>
+template <int BQ, int HP, int BK_, int LIST_>
 __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
-  using C = TCfg<BQ, HP, KSPLIT>;
+  using C = TCfg<BQ, HP, BK_, LIST_>;
   constexpr int D = C::D, MTW = C::MTW;
   // tile buffers K0, K1, V0, V1 (index 0-3), each C::TILE bytes
   __shared__ __attribute__((aligned(1024))) uint8_t stg[4][C::TILE];
@@ -107,14 +106,12 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   __shared__ int32_t lcol[C::LIST];
   __shared__ int32_t tflag[C::NTL];
   __shared__ int32_t qmin_s;
-  __shared__ float mrg_ml[KSPLIT == 2 ? C::NG : 1][2][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < C::NW);
   const int ln = lane & 31, hf = lane >> 5;
-  const int gi = wave % C::NG, kh = wave / C::NG;   // (head, query group) pair, key half
-  const int hd = gi / C::NQG, qg = gi % C::NQG;
+  const int hd = wave / C::NQG, qg = wave % C::NQG;   // this wavefront's head of the run and query group
   // the set whose slots and list this workgroup reads: set i, or with two
   // heads the i-th set of an even head (its partner head's set is identical)
   // (set counts are below 2^31: 32-bit index arithmetic)
@@ -156,7 +153,7 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   if (p.causal) {
     if (tid == 0) qmin_s = 0x7fffffff;
     __syncthreads();
-    if (kh == 0 && hd == 0 && qok) atomicMin(&qmin_s, qi);
+    if (hd == 0 && qok) atomicMin(&qmin_s, qi);
   }
 
   const rsrc_t qrs = make_rsrc(p.q + b * p.qs0 + h * p.qs1, ((int64_t)(N - 1) * p.qs2 + D) * 2);
@@ -204,13 +201,13 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   using B2 = std::integral_constant<int, 2>;
   using B3 = std::integral_constant<int, 3>;
 
-  // This wavefront's keys of a tile: M tiles kh MTW + jj (32 keys each).  K
+  // The keys of a tile: M tiles jj (32 keys each).  K
   // reads: the lane's score row of M tile t is key 32 t + key_of_row(ln);
   // chunk 2 ks + hf sits at (2 ks) ^ (hf ^ (key mod 16))
   int kbase[MTW], kx[MTW];
 #pragma unroll
   for (int jj = 0; jj < MTW; ++jj) {
-    const int kkey = 32 * (kh * MTW + jj) + key_of_row(ln);
+    const int kkey = 32 * jj + key_of_row(ln);
     kbase[jj] = kkey * (D * 2);
     kx[jj] = hf ^ (kkey & 15);
   }
@@ -251,7 +248,7 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
       for (int jj = 0; jj < MTW; ++jj)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int li = i * C::BK + 32 * (kh * MTW + jj) + 8 * hf + 16 * (e >> 3) + (e & 7);
+          const int li = i * C::BK + 32 * jj + 8 * hf + 16 * (e >> 3) + (e & 7);
           const int kp = li < n ? lcol[li] : -1;
           if (kp < 0 || kp >= N || (p.causal && kp > qi)) sc[jj][e] = -INFINITY;
         }
@@ -297,7 +294,7 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     for (int jj = 0; jj < MTW; ++jj)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int r0 = 32 * (kh * MTW + jj) + 16 * s2 + vrow0;   // keys of the first transpose read
+        const int r0 = 32 * jj + 16 * s2 + vrow0;   // keys of the first transpose read
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const int pos = (4 * (dt ^ vj)) | vcc;
@@ -365,53 +362,22 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
     }
   }
 
-  // with key halves, merge the two halves of every (head, query group) pair
-  // through LDS; normalise, store
-  const float l_w = halves_sum(l_run);
-  float m = m_run, l_tot = l_w, a1 = 1.f, a2 = 0.f;
-  const float *scratch = nullptr;
-  if constexpr (KSPLIT == 2) {
-    uint8_t *const mbuf = gi == 0 ? k0 : gi == 1 ? v0 : gi == 2 ? k1 : v1;
-    float *sc = reinterpret_cast<float *>(mbuf);
-    scratch = sc;
-    if (kh == 1) {
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4 *>(sc + ((dt * 4 + i4) * 64 + lane) * 4) =
-              f32x4{o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
-      mrg_ml[gi][0][lane] = m_run;
-      mrg_ml[gi][1][lane] = l_w;
-    }
-    __syncthreads();
-    if (kh != 0) return;
-    const float m2 = mrg_ml[gi][0][lane];
-    const float l2 = mrg_ml[gi][1][lane];
-    m = fmaxf(m_run, m2);
-    a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
-    l_tot = l_w * a1 + l2 * a2;
-  }
+  // normalise, store
+  const float l_tot = halves_sum(l_run);
+  const float m = m_run;
   // Normalised rows of this wavefront's 32 queries: staged in LDS as bf16
   // rows of 256 bytes (chunk c of row r at chunk position c ^ (r mod 16)),
   // then written out as whole rows, 16 lanes per row, instead of 16-byte
   // pieces of 32 rows per store (far fewer, full-line writes to drain
-  // before the workgroup ends).  The stage buffers are free: with key
-  // halves the merge used k0 and v0, and k1 takes the rows; otherwise every
+  // before the workgroup ends).  The stage buffers are free: every
   // wavefront is past the last tile.
-  uint8_t *const obuf = KSPLIT == 2 ? k1 + gi * 8192 : &stg[0][0] + wave * 8192;
+  uint8_t *const obuf = &stg[0][0] + wave * 8192;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       f32x4 x = {o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]};
-      if constexpr (KSPLIT == 2) {
-        const f32x4 o2 = *reinterpret_cast<const f32x4 *>(scratch + ((dt * 4 + i4) * 64 + lane) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = x[e] * a1 + o2[e] * a2;
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] *= inv;
       // dims 32 dt + 8 i4 + 4 hf .. +3: half hf of chunk 4 dt + i4 of row ln
@@ -429,19 +395,20 @@ __device__ __forceinline__ void attn_tok_body(const TokParams &p) {
   if (p.lse && hf == 0 && qok) p.lse[(int64_t)bh * N + qi] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
-// 64-query sets: 4 wavefronts (two query groups x key halves), two per CU;
-// 128-query sets and pairs of 64-query sets: 4 wavefronts that each take
-// whole tiles, two per CU; runs of four 64-query sets: 8 wavefronts, one per CU
-#define BSA_TOK_KERNEL(NAME, BQ, HP, KSPLIT)                                                        \
-  __global__ __attribute__((amdgpu_flat_work_group_size(TCfg<BQ, HP, KSPLIT>::NT, TCfg<BQ, HP, KSPLIT>::NT), \
+// 64-query sets: 2 wavefronts over 32-key tiles, four per CU; 128-query
+// sets and pairs of 64-query sets: 4 wavefronts over 64-key tiles, two per
+// CU; runs of four 64-query sets: 8 wavefronts, one per CU
+#define BSA_TOK_KERNEL(NAME, BQ, HP, BK, LIST)                                                       \
+  __global__ __attribute__((amdgpu_flat_work_group_size(TCfg<BQ, HP, BK, LIST>::NT,                  \
+                                                        TCfg<BQ, HP, BK, LIST>::NT),                 \
                             amdgpu_waves_per_eu(2, 2)))                                             \
   void NAME(const TokParams p) {                                                                   \
-    attn_tok_body<BQ, HP, KSPLIT>(p);                                                               \
+    attn_tok_body<BQ, HP, BK, LIST>(p);                                                             \
   }
-BSA_TOK_KERNEL(attn_tok_64, 64, 1, 2)
-BSA_TOK_KERNEL(attn_tok_128, 128, 1, 1)
-BSA_TOK_KERNEL(attn_tok_64x2, 64, 2, 1)
-BSA_TOK_KERNEL(attn_tok_64x4, 64, 4, 1)
+BSA_TOK_KERNEL(attn_tok_64, 64, 1, 32, 1024)
+BSA_TOK_KERNEL(attn_tok_128, 128, 1, 64, 2048)
+BSA_TOK_KERNEL(attn_tok_64x2, 64, 2, 64, 2048)
+BSA_TOK_KERNEL(attn_tok_64x4, 64, 4, 64, 2048)
 #undef BSA_TOK_KERNEL
 
 bool bad_strides(const int64_t s[3]) {
@@ -501,7 +468,7 @@ extern "C" int bsa_attn_tok_fwd(const bsa_tok_args *a, bsa_stream_t stream) {
   hipStream_t s = bsa_hip_stream(stream);
   if (a->kv_share == 4) hipLaunchKernelGGL(tok::attn_tok_64x4, dim3((unsigned)(n_sets / 4)), dim3(512), 0, s, p);
   else if (a->kv_share == 2) hipLaunchKernelGGL(tok::attn_tok_64x2, dim3((unsigned)(n_sets / 2)), dim3(256), 0, s, p);
-  else if (a->set_size == 64) hipLaunchKernelGGL(tok::attn_tok_64, dim3((unsigned)n_sets), dim3(256), 0, s, p);
+  else if (a->set_size == 64) hipLaunchKernelGGL(tok::attn_tok_64, dim3((unsigned)n_sets), dim3(128), 0, s, p);
   else hipLaunchKernelGGL(tok::attn_tok_128, dim3((unsigned)n_sets), dim3(256), 0, s, p);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
