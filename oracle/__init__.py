@@ -76,6 +76,8 @@ def lib():
         L.oracle_perm_from_labels.argtypes = [P, I64, I64, ctypes.c_int32, P]
         L.oracle_schedule.restype = ctypes.c_int
         L.oracle_schedule.argtypes = [P, P, I64, I64, I64, I64, I64, I64, P, I64, P]
+        L.oracle_schedule_pairs.restype = ctypes.c_int
+        L.oracle_schedule_pairs.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, P, P]
         L.oracle_spectral_order.restype = ctypes.c_int
         L.oracle_spectral_order.argtypes = [P, P, I64, I64, I64, I64, P, P]
         L.oracle_attn_rows.restype = ctypes.c_int
@@ -232,6 +234,28 @@ def schedule(row_ptr: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int, n
     if rc:
         raise ValueError("oracle_schedule failed: %d" % rc)
     return order
+
+
+def schedule_pairs(row_ptr: np.ndarray, col: np.ndarray, B: int, Hq: int, Hkv: int, nQB: int, W: int = 0,
+                   n_xcd: int = 1, row_perm: Optional[np.ndarray] = None, lw: Optional[np.ndarray] = None):
+    """Launch tables (order, order2) with consecutive query blocks of a head
+    that list identical blocks (and log-weights) paired in one entry; the
+    second row of a pair leaves an empty entry (-1, -1).  Buckets, adaptive
+    order (W = 0) and XCD deal as schedule()."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    lw = None if lw is None else np.ascontiguousarray(lw, dtype=np.float32)
+    if row_perm is not None:
+        row_perm = np.ascontiguousarray(row_perm, dtype=np.int32).reshape(-1)
+        assert row_perm.size == B * Hq * nQB
+    R = B * Hq * nQB
+    order = np.empty(R, dtype=np.int32)
+    order2 = np.empty(R, dtype=np.int32)
+    rc = lib().oracle_schedule_pairs(_p(row_ptr), _p(col), _p(lw), B, Hq, Hkv, nQB, W, n_xcd, _p(row_perm),
+                                     _p(order), _p(order2))
+    if rc:
+        raise ValueError("oracle_schedule_pairs failed: %d" % rc)
+    return order, order2
 
 
 def spectral_order(row_ptr: np.ndarray, col: np.ndarray, BH: int, nQB: int, nKB: int, iters: int):

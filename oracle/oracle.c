@@ -46,6 +46,14 @@
  *                     step of 2 only the first head of each pair of query
  *                     heads that share a KV head is scheduled (one launch
  *                     serves the pair's identical rows).
+ *  oracle_schedule_pairs
+ *                     The same sequence and buckets, with consecutive query
+ *                     blocks of a head that list identical blocks served by
+ *                     one launch entry (two rows, one staging of each K/V
+ *                     tile; the library's reading of the K/V-reuse motive of
+ *                     WaveAlign, section IV): greedy pairing along each head,
+ *                     entries sorted by their tile count, the second row of
+ *                     a pair leaving an empty entry at the bucket's end.
  *  oracle_spectral_order
  *                     WaveAlign stage 1 (section IV-C): rank-2 embedding of
  *                     each head's mask rows by matrix-free centred subspace
@@ -368,6 +376,147 @@ int oracle_schedule(const int32_t *row_ptr, const int32_t *col, int64_t B, int64
   free(sig);
   free(buf);
   free(logical);
+  return OR_OK;
+}
+
+/* Launch tables with paired rows.  The sequence, segments, buckets (W; 0
+ * takes 2048 and, with col, the adaptive order) and the XCD deal are those of
+ * oracle_schedule with head step 1.  Inside a bucket, positions i and i + G
+ * hold consecutive query blocks of one head (G = Hq / Hkv query heads per
+ * segment, head inner).  Walking the bucket's positions in ascending order,
+ * a position that is not already the second row of a pair is paired with
+ * position i + G when that position lies in the bucket and the two rows list
+ * the same blocks in the same order with the same log-weight bits (lw
+ * optional); otherwise it is a single entry.  An entry's cost is its tile
+ * count: nnz for a single row, 2 nnz for a pair.  Entries are ordered by
+ * (cost descending, position ascending); with the adaptive order, the
+ * signature cost of section "row schedule" above is taken over entries (the
+ * first row's signature) in that order and in position order, and when the
+ * position order is cheaper the entries keep it, sorted by (cost descending,
+ * position ascending) within each window of 64 positions.  The second rows
+ * of pairs follow as empty entries (-1, -1) in position order.  order[i]
+ * receives an entry's first row, order2[i] its second row or -1. */
+int oracle_schedule_pairs(const int32_t *row_ptr, const int32_t *col, const float *lw, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t nQB, int64_t W, int64_t n_xcd, const int32_t *row_perm,
+                          int32_t *order, int32_t *order2) {
+  if (!row_ptr || !col || !order || !order2 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || nQB <= 0 || W < 0)
+    return OR_ERR_ARG;
+  const int adaptive = W == 0;
+  if (W == 0) W = 2048;
+  const int64_t G = Hq / Hkv, R = B * Hq * nQB, seg = G * nQB;
+  int32_t *l1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  int32_t *l2 = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  int32_t *logical = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+  int8_t *kind = (int8_t *)malloc((size_t)W); /* 0 single, 1 first of a pair, 2 second */
+  key_idx *buf = (key_idx *)malloc(sizeof(key_idx) * (size_t)W);
+  int32_t *units = (int32_t *)malloc(sizeof(int32_t) * (size_t)W);
+  uint64_t *sig = (uint64_t *)calloc((size_t)W * 4, sizeof(uint64_t));
+  if (!l1 || !l2 || !logical || !kind || !buf || !units || !sig) return OR_ERR_ARG;
+  int64_t pos = 0;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t g = 0; g < Hkv; ++g)
+      for (int64_t u = 0; u < nQB; ++u)
+        for (int64_t j = 0; j < G; ++j) {
+          int64_t h = b * Hq + g * G + j;
+          int64_t uu = row_perm ? row_perm[h * nQB + u] : u;
+          logical[pos++] = (uu >= 0 && uu < nQB) ? (int32_t)(h * nQB + uu) : -1;
+        }
+  for (int64_t s0 = 0; s0 < R; s0 += seg) {
+    for (int64_t b0 = s0; b0 < s0 + seg; b0 += W) {
+      int64_t n = (b0 + W <= s0 + seg) ? W : s0 + seg - b0;
+      const int32_t *rw = logical + b0;
+      /* greedy pairing */
+      memset(kind, 0, (size_t)n);
+      for (int64_t i = 0; i < n; ++i) {
+        if (kind[i] == 2 || i + G >= n) continue;
+        int32_t a = rw[i], c = rw[i + G];
+        if (a < 0 || c < 0) continue;
+        int32_t la = row_ptr[a + 1] - row_ptr[a], lc = row_ptr[c + 1] - row_ptr[c];
+        int same = la == lc;
+        for (int32_t e = 0; same && e < la; ++e) {
+          if (col[row_ptr[a] + e] != col[row_ptr[c] + e]) same = 0;
+          if (lw) {
+            uint32_t x, y;
+            memcpy(&x, &lw[row_ptr[a] + e], 4);
+            memcpy(&y, &lw[row_ptr[c] + e], 4);
+            if (x != y) same = 0;
+          }
+        }
+        if (same) {
+          kind[i] = 1;
+          kind[i + G] = 2;
+        }
+      }
+      /* entries in position order, with their costs */
+      int64_t m = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        if (kind[i] == 2) continue;
+        int32_t r = rw[i];
+        int64_t nnz = r >= 0 ? row_ptr[r + 1] - row_ptr[r] : 0;
+        buf[m].key = -(kind[i] == 1 ? 2 * nnz : nnz);
+        buf[m].idx = (int32_t)i;
+        units[m] = (int32_t)i;
+        ++m;
+      }
+      qsort(buf, (size_t)m, sizeof(key_idx), cmp_key_idx);
+      if (adaptive) {
+        for (int64_t i = 0; i < n; ++i) {
+          uint64_t *si = sig + 4 * i;
+          si[0] = si[1] = si[2] = si[3] = 0;
+          int32_t r = rw[i];
+          if (r < 0) continue;
+          for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+            uint32_t bit = (uint32_t)col[e] % 256u;
+            si[bit / 64] |= 1ull << (bit % 64);
+          }
+        }
+        int64_t cost_sorted = 0, cost_seq = 0;
+        for (int64_t t = 0; t < m; ++t) {
+          cost_seq += sig_fresh(sig + 4 * units[t], t ? sig + 4 * units[t - 1] : NULL);
+          cost_sorted += sig_fresh(sig + 4 * buf[t].idx, t ? sig + 4 * buf[t - 1].idx : NULL);
+        }
+        if (cost_seq < cost_sorted) { /* position order, sorted within windows of 64 positions */
+          for (int64_t t = 0; t < m; ++t) {
+            int32_t i = units[t];
+            int32_t r = rw[i];
+            int64_t nnz = r >= 0 ? row_ptr[r + 1] - row_ptr[r] : 0;
+            buf[t].key = (int64_t)(i / 64) * ((int64_t)1 << 40) - (kind[i] == 1 ? 2 * nnz : nnz);
+            buf[t].idx = i;
+          }
+          qsort(buf, (size_t)m, sizeof(key_idx), cmp_key_idx);
+        }
+      }
+      int64_t t = 0;
+      for (; t < m; ++t) {
+        int32_t i = buf[t].idx;
+        l1[b0 + t] = rw[i];
+        l2[b0 + t] = kind[i] == 1 ? rw[i + G] : -1;
+      }
+      for (int64_t i = 0; i < n; ++i)
+        if (kind[i] == 2) {
+          l1[b0 + t] = -1;
+          l2[b0 + t] = -1;
+          ++t;
+        }
+    }
+  }
+  for (int64_t i = 0; i < R; ++i) {
+    int64_t src = i;
+    if (n_xcd > 1) {
+      int64_t x = i % n_xcd, k = i / n_xcd, start = 0;
+      for (int64_t y = 0; y < x; ++y) start += (R - 1 - y) / n_xcd + 1; /* launches on XCD y */
+      src = start + k;
+    }
+    order[i] = l1[src];
+    order2[i] = l2[src];
+  }
+  free(sig);
+  free(units);
+  free(buf);
+  free(kind);
+  free(logical);
+  free(l2);
+  free(l1);
   return OR_OK;
 }
 
