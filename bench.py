@@ -55,6 +55,10 @@ def parse():
                          "print them as one JSON line, and exit")
     ap.add_argument("--token-sets-only", action="store_true",
                     help="instead of the step: run only the token-level set measurements and print them")
+    ap.add_argument("--pair-rows-ab", default="",
+                    help="instead of the step: time the attention of the named workloads (comma-separated) "
+                         "with one row per launch entry and with identical consecutive rows paired, alternating, "
+                         "print one JSON line and exit")
     ap.add_argument("--kv-share-ab", action="store_true",
                     help="instead of the step: time the LLaMA-3.1-8B prefill workload's attention alone with "
                          "the per-head kernel and with the query-head-pair kernel (alternating, median of 20 "
@@ -134,6 +138,9 @@ def main():
     if args.kv_share_ab:
         print(json.dumps({"kv_share_ab": kv_share_ab(args, torch)}), flush=True)
         return
+    if args.pair_rows_ab:
+        print(json.dumps({"pair_rows_ab": pair_rows_ab(args, torch)}), flush=True)
+        return
 
     t0 = time.time()
     w = synth.CONFIGS[args.config]()
@@ -145,6 +152,7 @@ def main():
     # it also writes the LSE the oracle leg checks
     res = pipeline.forward(dw, n_xcd=args.n_xcd, wave_rows=args.wave_rows, overlap=True, want_lse=True)
     torch.cuda.synchronize()
+    head_kernel = attn_kernel_name(w.block, w.d, res.kv_share, res.order2 is not None)
     rp = res.row_ptr.cpu().numpy()
     col = res.col[:int(rp[-1])].cpu().numpy()   # col is sized by its bound
     stage1 = stage1_record(res)
@@ -271,7 +279,7 @@ def main():
                          **{"traffic_unit": "HBM-side bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
                             "frac_of_mfma_rate_random_bf16": round(
                                 attn_tflops / dev["mfma_random_bf16_operands"]["tflops"], 4),
-                            "kernel": attn_kernel_name(w.block, w.d),
+                            "kernel": head_kernel,
                             "per_unit": "4*d = 512 FLOP per allowed query-key pair",
                             "units_per_launch": pairs}),
         "cpu_baseline": cpu,
@@ -285,14 +293,17 @@ def main():
         sys.exit(3)
 
 
-def attn_kernel_name(block, d, kv_share=False):
+def attn_kernel_name(block, d, kv_share=False, pairs=False):
     """The attention kernel bsa_attn_fwd launches for dim-major V."""
     if kv_share:
         return "attn_ppg_128_%d" % d
+    if pairs and block == 128:
+        return "attn_ppx_128_%d" % d
     return ("attn_pp_128_%d" % d) if block == 128 else ("attn_dimv_%d_%d" % (block, d))
 
 
-ATTN_SOURCES = ("attn_pp.hip", "attn_ppg.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip", "bsa_internal.h")
+ATTN_SOURCES = ("attn_pp.hip", "attn_pp_body.h", "attn_ppg.hip", "attn_dimv.hip", "attn_common.h", "attn_fwd.hip",
+                "bsa_internal.h", "schedule.hip")
 
 
 def attn_sources_sha256():
@@ -331,14 +342,19 @@ def attention_alone(dw, args, torch, crm=False):
         k = api.permute_rows(dw.k, pk)
     v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
     share = kv_share_ok(dw, row_ptr, col, lw) and not crm
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
-                         head_step=2 if share else 1, col=col)
+    order2 = None
+    if not share and not crm and dw.block == 128:   # identical consecutive rows paired, as in the step
+        order, order2 = api.schedule_pairs(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                                           lw=lw)
+    else:
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                             head_step=2 if share else 1, col=col)
     out = torch.empty((dw.B, dw.Hq, dw.N, dw.d), dtype=q.dtype, device=q.device)
 
     def launch():   # the query gather and the output scatter are fused into the kernel
         api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
                      gather_perm_q=pq, causal=dw.causal, v_dim_major=True, out=out, crm=crm_rows,
-                     kv_share=share)
+                     kv_share=share, order2=order2)
 
     for _ in range(10):
         launch()
@@ -489,6 +505,71 @@ def kv_share_ab(args, torch):
                     "frac": round(flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     log("kv_share A/B: per head %.3f ms, head pairs %.3f ms" % (res["per_head"]["median_ms"],
                                                                 res["head_pairs"]["median_ms"]))
+    return res
+
+
+def pair_rows_ab(args, torch):
+    """Attention alone (query gather and output scatter fused) on each named
+    workload with one row per launch entry (bsa_schedule, attn_pp) and with
+    identical consecutive rows paired (bsa_schedule_pairs, attn_ppx): both on
+    the same inputs, alternating, 10 warm-up rounds and 20 timed launches
+    each; the outputs are compared (the same function up to rounding
+    order)."""
+    from block_sparse_attention_mask_amd import api, metrics, pipeline
+    import synth
+    res = {}
+    for cfg in args.pair_rows_ab.split(","):
+        w = synth.CONFIGS[cfg]()
+        dw = pipeline.to_device(w, torch.device("cuda"))
+        row_ptr, col, lw = api.build_csr(dw.mask, dw.T, dw.p, dw.lw_map, dw.nQB, dw.force_diag)
+        q, k, pq, pk = dw.q, dw.k, None, None
+        if dw.permuted:
+            pq = api.perm_from_labels(dw.labels_q, dw.n_clusters)
+            pk = api.perm_from_labels(dw.labels_k, dw.n_clusters)
+            k = api.permute_rows(dw.k, pk)
+        v = api.transpose_rows(dw.v, pk, ld=dw.nQB * dw.block)
+        tables = {"rows": (api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, col=col),
+                           None),
+                  "pairs": api.schedule_pairs(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                                              lw=lw)}
+        outs, launches = {}, {}
+        for key, (o, o2) in tables.items():
+            out = torch.empty((dw.B, dw.Hq, dw.N, dw.d), dtype=q.dtype, device=q.device)
+            outs[key] = out
+            launches[key] = (lambda o=o, o2=o2, out=out: api.attn_fwd(
+                q, k, v, row_ptr, col, dw.block, lw=lw, order=o, order2=o2, scatter_perm_q=pq, gather_perm_q=pq,
+                causal=dw.causal, v_dim_major=True, out=out))
+        s = torch.cuda.current_stream()
+        for _ in range(10):
+            for key in launches:
+                launches[key]()
+        ms = {key: [] for key in launches}
+        for _ in range(20):
+            for key in launches:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                launches[key]()
+                b.record(s)
+                torch.cuda.synchronize()
+                ms[key].append(a.elapsed_time(b))
+        rp = row_ptr.cpu().numpy()
+        nnz = int(rp[-1])
+        pairs = metrics.count_pairs(rp, col[:nnz].cpu().numpy(), w.N, w.block, w.causal)
+        flop = 4.0 * w.d * pairs
+        as_f32 = lambda t: (t.view(torch.bfloat16) if t.dtype in (torch.int16, torch.uint16) else t).float()
+        diff = (as_f32(outs["rows"]) - as_f32(outs["pairs"])).abs()
+        r = {"workload": workload_name(cfg), "launch_entries": int(rp.size - 1),
+             "pair_entries": int((tables["pairs"][1] >= 0).sum().item()),
+             "max_abs_diff": float(diff.max().item()), "mean_abs_diff": float(diff.mean().item())}
+        for key, kern in (("rows", attn_kernel_name(w.block, w.d)), ("pairs", attn_kernel_name(w.block, w.d, pairs=True))):
+            t = float(np.median(ms[key]))
+            r[key] = {"kernel": kern, "median_ms": round(t, 4), "tflops": round(flop / (t * 1e-3) / 1e12, 2),
+                      "frac": round(flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log("%s: one row per entry %.3f ms, pairs %.3f ms (%d pair entries)" % (
+            cfg, r["rows"]["median_ms"], r["pairs"]["median_ms"], r["pair_entries"]))
+        res[cfg] = r
+        del dw, outs, launches, q, k, v
+        torch.cuda.empty_cache()
     return res
 
 
@@ -693,7 +774,7 @@ def summarize_profile(d):
     import csv
     import glob
     import statistics
-    ksub = "attn_pp_128_128("
+    ksub = "attn_ppx_128_128("
 
     def rows(sub, suffix):
         f = glob.glob(os.path.join(d, sub, "*" + suffix))
@@ -728,7 +809,7 @@ def summarize_profile(d):
     h, m = statistics.mean(hits), statistics.mean(miss)
     rec = {
         "workload": "Wan2.1-14B clustered, 1x40x75600, d128, 128x128 blocks, 15.0% density",
-        "kernel": "attn_pp_128_128",
+        "kernel": "attn_ppx_128_128",
         "kernel_sources_sha256": attn_sources_sha256(),
         "dispatches_counted": len(f),
         "fetch_kib_per_launch": round(fk, 2), "write_kib_per_launch": round(wk, 2),
@@ -803,11 +884,16 @@ def stage_times(pipeline, dw, args, torch):
         row_perm, _ = api.spectral_order(row_ptr, col, dw.B * dw.Hq, dw.nQB, dw.nQB, 10, enable=dec)
     share = kv_share_ok(dw, row_ptr, col, lw)
     ev[3].record(s)
-    order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm,
-                         head_step=2 if share else 1, col=col)
+    order2 = None
+    if not share and dw.block == 128:
+        order, order2 = api.schedule_pairs(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd,
+                                           lw=lw, row_perm=row_perm)
+    else:
+        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, args.wave_rows, args.n_xcd, row_perm=row_perm,
+                             head_step=2 if share else 1, col=col)
     ev[4].record(s)
     api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=pq,
-                 gather_perm_q=pq, causal=dw.causal, v_dim_major=True, kv_share=share)
+                 gather_perm_q=pq, causal=dw.causal, v_dim_major=True, kv_share=share, order2=order2)
     ev[5].record(s)
     torch.cuda.synchronize()
     names = ["mask_to_csr", "perm_k_gather_and_v_transpose", "stage1_adaptive_skip", "schedule",
@@ -952,7 +1038,8 @@ def workload_line(cfg, args, torch, with_oracle=True):
                       "block": w.block, "causal": bool(w.causal), "permuted": bool(w.permuted),
                       "log_weights": w.lw_map is not None},
             "nnz_blocks": nnz, "block_density": round(nnz / float(w.R * w.nKB), 5), "allowed_pairs": int(pairs),
-            "effective_gflop": round(flop / 1e9, 3), "kernel": attn_kernel_name(w.block, w.d, res.kv_share),
+            "effective_gflop": round(flop / 1e9, 3),
+            "kernel": attn_kernel_name(w.block, w.d, res.kv_share, res.order2 is not None),
             "kv_share": bool(res.kv_share),
             "kernel_alone_median50_ms": solo["median_ms"], "l2_flushed_ms": solo["flushed_ms"],
             "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),

@@ -24,7 +24,7 @@ EXPORTS = ("bsa_version", "bsa_strerror", "bsa_csr_count", "bsa_csr_fill", "bsa_
            "bsa_crm_to_csr", "bsa_segment_offsets", "bsa_segment_means", "bsa_is_sample", "bsa_perm_from_labels",
            "bsa_permute_rows", "bsa_unpermute_rows", "bsa_transpose_rows", "bsa_spectral_order", "bsa_schedule",
            "bsa_attn_fwd", "bsa_attn_tok_fwd", "bsa_group_mass", "bsa_topk_rows", "bsa_stage1_decide",
-           "bsa_stage1_default_params", "bsa_pair_rows_equal",
+           "bsa_stage1_default_params", "bsa_pair_rows_equal", "bsa_schedule_pairs",
            "bsa_device_cus", "bsa_device_clock_khz", "bsa_clock_probe")
 
 
@@ -43,6 +43,7 @@ class AttnArgs(ctypes.Structure):
         ("crm", P),
         ("gather_perm_q", P),
         ("kv_share", I32),
+        ("order2", P),
     ]
 
 
@@ -129,6 +130,8 @@ def load():
         L.bsa_transpose_rows.argtypes = [P, P, P, I32, I32, I64, I32, I64, P, P, P]
         L.bsa_schedule.restype = ctypes.c_int
         L.bsa_schedule.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P, I32, P, P]
+        L.bsa_schedule_pairs.restype = ctypes.c_int
+        L.bsa_schedule_pairs.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]
         L.bsa_pair_rows_equal.restype = ctypes.c_int
         L.bsa_pair_rows_equal.argtypes = [P, P, P, I32, I32, I32, I32, P, P]
         L.bsa_spectral_order.restype = ctypes.c_int

@@ -333,6 +333,29 @@ def schedule(row_ptr: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int, wave_ro
     return order
 
 
+def schedule_pairs(row_ptr: torch.Tensor, col: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int,
+                   wave_rows: int = 0, n_xcd: int = 8, lw: Optional[torch.Tensor] = None,
+                   row_perm: Optional[torch.Tensor] = None, stream=None):
+    """Launch tables (order, order2) for attn_fwd(order=..., order2=...):
+    consecutive query blocks of a head whose lists (and log-weights) are
+    identical share one entry; the second row of a pair leaves an empty entry
+    (-1, -1) at the end of its bucket.  Buckets and order as schedule()."""
+    _dev(row_ptr, "row_ptr", torch.int32)
+    _dev(col, "col", torch.int32)
+    if lw is not None:
+        _dev(lw, "lw", torch.float32)
+    if row_perm is not None:
+        _dev(row_perm, "row_perm", torch.int32)
+        if row_perm.numel() != B * Hq * nQB:
+            raise ValueError("row_perm must hold B*Hq*nQB entries")
+    order = torch.empty(B * Hq * nQB, dtype=torch.int32, device=row_ptr.device)
+    order2 = torch.empty_like(order)
+    check("bsa_schedule_pairs", load().bsa_schedule_pairs(_ptr(row_ptr), _ptr(col), _ptr(lw), B, Hq, Hkv, nQB,
+                                                          int(wave_rows), int(n_xcd), _ptr(row_perm),
+                                                          _ptr(order), _ptr(order2), _stream(stream)))
+    return order, order2
+
+
 def pair_rows_equal(row_ptr: torch.Tensor, col: torch.Tensor, B: int, Hq: int, Hkv: int, nQB: int,
                     lw: Optional[torch.Tensor] = None, equal: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
@@ -418,7 +441,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = False, scale: float = 0.0, causal: bool = False,
              v_dim_major: bool = False, crm: Optional[torch.Tensor] = None,
-             gather_perm_q: Optional[torch.Tensor] = None, kv_share: bool = False, stream=None):
+             gather_perm_q: Optional[torch.Tensor] = None, kv_share: bool = False,
+             order2: Optional[torch.Tensor] = None, stream=None):
     """Block-sparse attention forward; returns (out, lse or None).  With
     ``v_dim_major`` v is [B][Hkv][d][ld] (keys contiguous, from transpose_rows),
     otherwise [B][Hkv][N][d].  With ``crm`` (CRM rows from crm_build) the lists
@@ -427,7 +451,9 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
     gather_perm_q[bh][i] for permuted position i.  With ``kv_share`` the rows
     of query heads 2j and 2j + 1 of every KV group must be identical
     (pair_rows_equal checks it): one launch serves both, and order, if given,
-    comes from schedule(..., head_step=2)."""
+    comes from schedule(..., head_step=2).  With ``order2`` (beside order,
+    same length) launch entry i also serves row order2[i] when it is a row:
+    the two rows list identical blocks (schedule_pairs builds such tables)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, _BF16_LIKE)
     B, Hq, N, d = q.shape
@@ -455,6 +481,11 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: Optiona
     a.crm = _ptr(crm)
     a.gather_perm_q = _ptr(gather_perm_q)
     a.kv_share = 2 if kv_share else 0
+    if order2 is not None:
+        _dev(order2, "order2", (torch.int32,))
+        if order is None or order2.numel() != order.numel():
+            raise ValueError("order2 needs order, with as many entries")
+    a.order2 = _ptr(order2)
     check("bsa_attn_fwd", load().bsa_attn_fwd(ctypes.byref(a), _stream(stream)))
     return out, lse
 

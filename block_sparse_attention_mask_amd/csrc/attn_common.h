@@ -28,12 +28,24 @@ struct AttnParams {
   uint32_t crm_tail;     // bits of a row's last word that name KV blocks
   const float *lw;
   const int32_t *order;
+  const int32_t *order2;  // second row of a launch entry (identical pair), or null
   const int32_t *sperm;
   const int32_t *gperm;  // query gather: permuted position -> row of q, or null
   int64_t N, R;
   int Hq, G, nQB, causal;
   float c;  // softmax scale * log2(e)
 };
+
+// The AttnParams of a kernel whose first argument it is, read through its
+// kernel-argument block: the pointer passes through an empty asm statement,
+// so each field is loaded where it is read (scalar loads) instead of being
+// held in a scalar register from the kernel's start.
+typedef const __attribute__((address_space(4))) AttnParams *kparams_t;
+__device__ __forceinline__ kparams_t kernel_params() {
+  kparams_t pk = (kparams_t)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(pk));
+  return pk;
+}
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   f32x2 f = {a, b};
@@ -128,5 +140,6 @@ hipError_t launch_attn_tokv(const AttnParams &p, int block, int d, int64_t grid,
 hipError_t launch_attn_dimv(const AttnParams &p, int block, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_pp(const AttnParams &p, int d, int64_t grid, hipStream_t s);
 hipError_t launch_attn_ppg(const AttnParams &p, int d, int64_t grid, hipStream_t s);
+hipError_t launch_attn_ppx(const AttnParams &p, int d, int64_t grid, hipStream_t s);
 
 }  // namespace bsa

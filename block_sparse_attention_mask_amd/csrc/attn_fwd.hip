@@ -1,7 +1,8 @@
 // bsa_attn_fwd: argument checks and dispatch to the attention kernels
 // (dim-major V: attn_pp.hip for 128-key blocks, attn_dimv.hip for 64, and
 // attn_ppg.hip for pairs of query heads that share K/V and their lists;
-// token-major V: attn_tokv.hip).  Lists come as CSR or as CRM rows; the
+// token-major V: attn_tokv.hip; launch entries of rows and identical row
+// pairs: attn_ppx in attn_ppg.hip).  Lists come as CSR or as CRM rows; the
 // dim-major kernels have a variant for each.
 #include "attn_common.h"
 
@@ -47,6 +48,10 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
     return BSA_ERR_ARG;
   }
   if (a->kv_share != 0 && a->kv_share != 2) return BSA_ERR_ARG;
+  // launch entries that serve a row or an identical pair of rows
+  if (a->order2 && !a->order) return BSA_ERR_ARG;
+  if (a->order2 && (a->kv_share || a->crm || a->v_layout != BSA_V_DIM_MAJOR || a->block != 128))
+    return BSA_ERR_UNSUPPORTED;
   const int G = a->Hq / a->Hkv;
   if (a->kv_share == 2 && (G % 2 || a->crm || a->v_layout != BSA_V_DIM_MAJOR || a->block != 128))
     return BSA_ERR_UNSUPPORTED;
@@ -73,6 +78,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   p.crm_tail = bsa_crm_tail((int)nQB);
   p.lw = a->lw;
   p.order = a->order;
+  p.order2 = a->order2;
   p.sperm = a->scatter_perm_q;
   p.gperm = a->gather_perm_q;
   p.N = a->N;
@@ -88,6 +94,7 @@ extern "C" int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream) {
   hipError_t err;
   if (a->v_layout == BSA_V_TOKEN_MAJOR) err = bsa::launch_attn_tokv(p, a->block, a->d, grid, s);
   else if (a->kv_share == 2) err = bsa::launch_attn_ppg(p, a->d, grid, s);
+  else if (a->order2) err = bsa::launch_attn_ppx(p, a->d, grid, s);
   else if (a->block == 128) err = bsa::launch_attn_pp(p, a->d, grid, s);
   else err = bsa::launch_attn_dimv(p, a->block, a->d, grid, s);
   return err == hipSuccess ? BSA_OK : BSA_ERR_HIP;

@@ -35,7 +35,7 @@
 //     2^-60 is recomputed from its cold tiles' max) are those of attn_pp.hip.
 #include <type_traits>
 
-#include "attn_common.h"
+#include "attn_pp_body.h"
 
 namespace bsa {
 namespace ppg {
@@ -60,42 +60,40 @@ struct GCfg {
   static_assert((2 * MTW) % NSLOT == 0 || NSLOT % (2 * MTW) == 0, "copies spread evenly over the softmax step");
 };
 
+// LDS of one workgroup: K buffers 0-2, V^T buffers 3-5, each C::KB bytes at
+// byte i * C::KB of smem; the staged list; the redo votes.
 template <int D>
-__device__ __forceinline__ void attn_ppg_body(const AttnParams &p, const int32_t *__restrict__ row_ptr,
+struct PgShared {
+  alignas(1024) uint8_t smem[6 * GCfg<D>::KB];
+  int32_t lcol[GCfg<D>::LIST];
+  float lbias[GCfg<D>::LIST];
+  int redo_vote[GCfg<D>::NW];
+};
+
+// Rows r0 and r1 (in [0, R), same batch and KV head, identical lists: the
+// list of r0 is read), computed with the LDS arrays given: wavefronts 0-3
+// serve r0, wavefronts 4-7 r1.
+template <int D>
+__device__ __forceinline__ void attn_ppg_body(const AttnParams &p, uint8_t *__restrict__ const smem,
+                                              int32_t *__restrict__ const lcol, float *__restrict__ const lbias,
+                                              int *__restrict__ const redo_vote, const int32_t r0, const int32_t r1,
+                                              const int32_t *__restrict__ row_ptr,
                                               const int32_t *__restrict__ col, const float *__restrict__ lw,
-                                              const int32_t *__restrict__ order,
                                               const int32_t *__restrict__ sperm, uint16_t *__restrict__ out,
                                               float *__restrict__ lse) {
   using C = GCfg<D>;
-  // LDS: K buffers 0-2, V^T buffers 3-5, each C::KB bytes at byte i * C::KB
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[6 * C::KB];
-  __shared__ int32_t lcol[C::LIST];
-  __shared__ float lbias[C::LIST];
-  __shared__ int redo_vote[C::NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < C::NW);
   const int ln = lane & 31, hf = lane >> 5;
   const int qg = wave % C::NQG, hd = wave / C::NQG;
-  // the pair's row of its first head: from the launch table (rows of even
-  // heads only), or launch index i -> pair-row i
-  int32_t r0;
-  if (order) {
-    r0 = order[blockIdx.x];
-  } else {
-    const int64_t i = blockIdx.x, pr = i / p.nQB;
-    r0 = (int32_t)(2 * pr * p.nQB + (i - pr * p.nQB));
-  }
-  if (r0 < 0 || r0 >= p.R) return;   // a launch-table entry outside the rows computes nothing
-  const int64_t bh0 = r0 / p.nQB;
-  const int u = (int)(r0 - bh0 * p.nQB);
-  const int64_t b = bh0 / p.Hq;
-  const int h0 = (int)(bh0 - b * p.Hq);
-  if (h0 & 1) return;                // not the first head of a pair
-  const int h = h0 + hd;
-  const int64_t bh = bh0 + hd;
-  const int g = h0 / p.G;
+  const int32_t rw = hd ? r1 : r0;   // this wavefront's row
+  const int64_t bh = rw / p.nQB;
+  const int u = (int)(rw - bh * p.nQB);
+  const int64_t b = bh / p.Hq;
+  const int h = (int)(bh - b * p.Hq);
+  const int g = h / p.G;
   const int N = (int)p.N;
   const int e0 = row_ptr[r0], e1 = row_ptr[r0 + 1];
   const int nfull = N / C::BLK;
@@ -432,18 +430,74 @@ __device__ __forceinline__ void attn_ppg_body(const AttnParams &p, const int32_t
   else run(std::integral_constant<int, 1>());
 }
 
+// Pairs of query heads: launch entry i serves the row of an even head (the
+// launch table's entry, or pair-row i) and the same query block of the next
+// head.  An entry outside the rows, or a row of an odd head, computes
+// nothing.
 #define BSA_PPG_KERNEL(NAME, D)                                                                      \
   __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))     \
   void NAME(const AttnParams p, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col, \
             const float *__restrict__ lw, const int32_t *__restrict__ order,                         \
             const int32_t *__restrict__ sperm, uint16_t *__restrict__ out, float *__restrict__ lse) { \
-    attn_ppg_body<D>(p, row_ptr, col, lw, order, sperm, out, lse);                                 \
+    __shared__ PgShared<D> sh;                                                                      \
+    int32_t r0;                                                                                     \
+    if (order) {                                                                                    \
+      r0 = order[blockIdx.x];                                                                       \
+    } else {                                                                                        \
+      const int64_t i = blockIdx.x, pr = i / p.nQB;                                                 \
+      r0 = (int32_t)(2 * pr * p.nQB + (i - pr * p.nQB));                                           \
+    }                                                                                               \
+    if (r0 < 0 || r0 >= p.R) return;                                                                \
+    if (((r0 / p.nQB) % p.Hq) & 1) return;                                                          \
+    attn_ppg_body<D>(p, sh.smem, sh.lcol, sh.lbias, sh.redo_vote, r0, r0 + p.nQB, row_ptr, col, lw, sperm, \
+                     out, lse);                                                                     \
   }
 BSA_PPG_KERNEL(attn_ppg_128_128, 128)
 BSA_PPG_KERNEL(attn_ppg_128_64, 64)
 #undef BSA_PPG_KERNEL
 
+// Rows and identical pairs in one launch: entry i serves row order[i] alone
+// (the key-half body of attn_pp_body.h) or, when order2[i] is a row,
+// together with row order2[i], which lists the same blocks (the pair body
+// above; both bodies share one LDS allocation).  An entry outside the rows
+// computes nothing.
+template <int D>
+union MixShared {
+  pp::PpShared<D> one;
+  PgShared<D> two;
+};
+#define BSA_PPX_KERNEL(NAME, D)                                                                      \
+  __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))     \
+  void NAME(const AttnParams p, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col, \
+            const float *__restrict__ lw, const int32_t *__restrict__ order,                         \
+            const int32_t *__restrict__ order2, const int32_t *__restrict__ sperm,                  \
+            uint16_t *__restrict__ out, float *__restrict__ lse) {                                  \
+    __shared__ MixShared<D> sh;                                                                     \
+    const int32_t r0 = order[blockIdx.x];                                                           \
+    const int32_t r1 = order2[blockIdx.x];                                                          \
+    if (r0 < 0 || r0 >= p.R) return;                                                                \
+    if (r1 >= 0 && r1 < p.R)                                                                        \
+      attn_ppg_body<D>(p, sh.two.smem, sh.two.lcol, sh.two.lbias, sh.two.redo_vote, r0, r1, row_ptr, col, \
+                       lw, sperm, out, lse);                                                        \
+    else                                                                                            \
+      pp::attn_pp_body<D, false>(p, sh.one, r0, row_ptr, col, lw, sperm, out, lse);                 \
+  }
+BSA_PPX_KERNEL(attn_ppx_128_128, 128)
+BSA_PPX_KERNEL(attn_ppx_128_64, 64)
+#undef BSA_PPX_KERNEL
+
 }  // namespace ppg
+
+hipError_t launch_attn_ppx(const AttnParams &p, int d, int64_t grid, hipStream_t s) {
+  const dim3 g((unsigned)grid), t(512);
+  if (d == 128)
+    hipLaunchKernelGGL(ppg::attn_ppx_128_128, g, t, 0, s, p, p.row_ptr, p.col, p.lw, p.order, p.order2, p.sperm,
+                       p.o, p.lse);
+  else
+    hipLaunchKernelGGL(ppg::attn_ppx_128_64, g, t, 0, s, p, p.row_ptr, p.col, p.lw, p.order, p.order2, p.sperm,
+                       p.o, p.lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_ppg(const AttnParams &p, int d, int64_t grid, hipStream_t s) {
   const dim3 g((unsigned)grid), t(512);

@@ -39,6 +39,15 @@
 // bsa_pair_rows_equal checks the precondition of that pair kernel: one
 // wavefront per pair of rows compares lengths, block indices and log-weight
 // bits, and clears a flag on any difference.
+//
+// bsa_schedule_pairs builds launch tables in which consecutive query blocks
+// of a head with identical lists share one entry (the attention kernel then
+// stages each K/V tile once for both rows).  Per bucket: each position
+// compares its row with the same head's next one (lengths, signatures, then
+// block indices and log-weight bits); one thread per head pairs greedily
+// along its positions; the entries are keyed by tile count (2 nnz for a
+// pair) and sorted as above, the adaptive choice taking each entry's first
+// row; the second rows of pairs follow as empty entries.
 #include "bsa_internal.h"
 
 namespace {
@@ -177,6 +186,187 @@ __global__ __launch_bounds__(1024) void schedule_kernel(const int32_t *__restric
   }
 }
 
+// Paired launch tables (bsa_schedule_pairs): one workgroup per bucket of a
+// (b, g) segment (head step 1, so G positions per query block, head inner).
+__global__ __launch_bounds__(1024) void schedule_pairs_kernel(const int32_t *__restrict__ row_ptr,
+                                                              const int32_t *__restrict__ col,
+                                                              const float *__restrict__ lw, int Hq, int Hkv,
+                                                              int nQB, int W, int adaptive, int n_xcd, int64_t R,
+                                                              const int32_t *__restrict__ row_perm,
+                                                              int32_t *__restrict__ order,
+                                                              int32_t *__restrict__ order2) {
+  __shared__ uint64_t key[kMaxWave];
+  __shared__ uint64_t sig[kMaxWave][4];
+  __shared__ int32_t rlen[kMaxWave];
+  __shared__ int16_t upos[kMaxWave];       // entries in position order (adaptive cost)
+  __shared__ int8_t same[kMaxWave], kind[kMaxWave];   // kind: 0 alone, 1 first of a pair, 2 second
+  __shared__ int cost[2];
+  __shared__ int n_units;
+  const int G = Hq / Hkv;
+  const int64_t seg = (int64_t)G * nQB;
+  const int64_t nbk = (seg + W - 1) / W;
+  const int64_t s = blockIdx.x / nbk, k = blockIdx.x % nbk;
+  const int64_t start = s * seg + k * W;
+  const int n = (int)((k + 1) * W <= seg ? W : seg - k * W);
+  int P2 = 1;
+  while (P2 < n) P2 <<= 1;
+  const int64_t b = s / Hkv, g = s % Hkv;
+  auto row_at = [&](int64_t j) -> int64_t {
+    const int64_t p = j / G, h = b * Hq + g * G + j % G;
+    const int64_t u = row_perm ? (int64_t)row_perm[h * nQB + p] : p;
+    return (u >= 0 && u < nQB) ? h * nQB + u : -1;
+  };
+  // rows, lengths, signatures
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int64_t r = row_at(k * W + i);
+    uint64_t sg[4] = {0, 0, 0, 0};
+    int32_t len = 0;
+    if (r >= 0) {
+      const int32_t e1 = row_ptr[r + 1];
+      int32_t e = row_ptr[r];
+      len = e1 - e;
+      auto add = [&](int32_t v) {
+        const uint32_t bit = (uint32_t)v & 255u;
+        sg[bit >> 6] |= 1ull << (bit & 63);
+      };
+      for (; e + 8 <= e1; e += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = col[e + j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) add(v[j]);
+      }
+      for (; e < e1; ++e) add(col[e]);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sig[i][w] = sg[w];
+    rlen[i] = r >= 0 ? len : -1;
+  }
+  if (threadIdx.x < 2) cost[threadIdx.x] = 0;
+  __syncthreads();
+  // does position i list what the same head's next position lists?
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    bool eq = false;
+    const int c = i + G;
+    if (c < n && rlen[i] >= 0 && rlen[i] == rlen[c] && sig[i][0] == sig[c][0] && sig[i][1] == sig[c][1] &&
+        sig[i][2] == sig[c][2] && sig[i][3] == sig[c][3]) {
+      const int64_t ra = row_at(k * W + i), rc = row_at(k * W + c);
+      const int32_t a0 = row_ptr[ra], c0 = row_ptr[rc], len = rlen[i];
+      eq = true;
+      for (int32_t e = 0; eq && e < len; ++e) {
+        eq = col[a0 + e] == col[c0 + e];
+        if (lw) eq = eq && __float_as_uint(lw[a0 + e]) == __float_as_uint(lw[c0 + e]);
+      }
+    }
+    same[i] = eq ? 1 : 0;
+  }
+  __syncthreads();
+  // greedy pairing, one thread per head of the segment
+  if (threadIdx.x < G) {
+    bool second = false;
+    for (int i = threadIdx.x; i < n; i += G) {
+      int8_t kd = 0;
+      if (second) {
+        kd = 2;
+        second = false;
+      } else if (same[i]) {
+        kd = 1;
+        second = true;
+      }
+      kind[i] = kd;
+    }
+  }
+  __syncthreads();
+  auto cost_of = [&](int i) -> uint32_t {
+    const int32_t len = rlen[i] > 0 ? rlen[i] : 0;
+    return (uint32_t)(kind[i] == 1 ? 2 * len : len);
+  };
+  for (int i = threadIdx.x; i < P2; i += 1024) {
+    uint64_t kk = ~0ull;
+    if (i < n)
+      kk = kind[i] == 2 ? ((1ull << 63) | (uint32_t)i)
+                        : (((uint64_t)(0x7fffffffu - cost_of(i)) << 32) | (uint32_t)i);
+    key[i] = kk;
+  }
+  __syncthreads();
+  auto sort_keys = [&]() {
+    for (int size = 2; size <= P2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = threadIdx.x; i < P2 / 2; i += 1024) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t a = key[lo], c = key[hi];
+          if ((a > c) == up) {
+            key[lo] = c;
+            key[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  };
+  sort_keys();
+  bool keep_seq = false;
+  if (adaptive) {
+    if (threadIdx.x == 0) {   // the entries in position order
+      int m = 0;
+      for (int i = 0; i < n; ++i)
+        if (kind[i] != 2) upos[m++] = (int16_t)i;
+      n_units = m;
+    }
+    __syncthreads();
+    const int m = n_units;
+    int cs = 0, cq = 0;
+    for (int t = threadIdx.x; t < m; t += 1024) {
+      const int a = (int)(key[t] & 0xffffffffu), pa = t ? (int)(key[t - 1] & 0xffffffffu) : 0;
+      cs += sig_fresh(sig[a], t ? sig[pa] : nullptr);
+      cq += sig_fresh(sig[upos[t]], t ? sig[upos[t - 1]] : nullptr);
+    }
+    atomicAdd(&cost[0], cs);
+    atomicAdd(&cost[1], cq);
+    __syncthreads();
+    keep_seq = cost[1] < cost[0];
+    if (keep_seq) {
+      // position order, longest-first within windows of kSeqWave positions:
+      // keys (window, INT32_MAX - cost, position) in 6 + 31 + 12 bits; the
+      // second rows of pairs in window 63, after every entry
+      __syncthreads();
+      for (int i = threadIdx.x; i < P2; i += 1024) {
+        uint64_t kk = ~0ull;
+        if (i < n)
+          kk = kind[i] == 2 ? ((63ull << 43) | (uint32_t)i)
+                            : (((uint64_t)(i / kSeqWave) << 43) |
+                               ((uint64_t)(0x7fffffffu - cost_of(i)) << 12) | (uint32_t)i);
+        key[i] = kk;
+      }
+      __syncthreads();
+      sort_keys();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int src = (int)(key[i] & (keep_seq ? 0xfffu : 0xffffffffu));
+    int32_t r = -1, r2 = -1;
+    if (kind[src] != 2) r = (int32_t)row_at(k * W + src);
+    if (kind[src] == 1) r2 = (int32_t)row_at(k * W + src + G);
+    const int64_t P = start + i;
+    int64_t launch = P;
+    if (n_xcd > 1) {
+      int64_t st = 0;
+      for (int x = 0; x < n_xcd; ++x) {
+        const int64_t cnt = x < R ? (R - 1 - x) / n_xcd + 1 : 0;
+        if (P < st + cnt) {
+          launch = (P - st) * n_xcd + x;
+          break;
+        }
+        st += cnt;
+      }
+    }
+    order[launch] = r;
+    order2[launch] = r2;
+  }
+}
+
 __global__ void flag_set_kernel(int32_t *__restrict__ flag) {
   if (threadIdx.x == 0) flag[0] = 1;
 }
@@ -234,6 +424,26 @@ extern "C" int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t 
   // the order choice applies to whole-segment buckets (wave_rows = 0)
   hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream),
                      row_ptr, wave_rows ? nullptr : col, Hq, Hkv, nQB, W, n_xcd, R, row_perm, head_step, order);
+  BSA_LAUNCH_CHECK();
+  return BSA_OK;
+}
+
+extern "C" int bsa_schedule_pairs(const int32_t *row_ptr, const int32_t *col, const float *lw, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t nQB, int32_t wave_rows, int32_t n_xcd,
+                                  const int32_t *row_perm, int32_t *order, int32_t *order2,
+                                  bsa_stream_t stream) {
+  if (!row_ptr || !col || !order || !order2 || B <= 0 || Hq <= 0 || Hkv <= 0 || nQB <= 0) return BSA_ERR_ARG;
+  if (Hq % Hkv) return BSA_ERR_ARG;
+  if (wave_rows < 0 || n_xcd < 0 || n_xcd > 64) return BSA_ERR_ARG;
+  if (wave_rows > kMaxWave) return BSA_ERR_UNSUPPORTED;
+  const int64_t R = (int64_t)B * Hq * nQB;
+  if (R >= (int64_t(1) << 31)) return BSA_ERR_UNSUPPORTED;
+  const int W = wave_rows ? wave_rows : kMaxWave;
+  if (Hq / Hkv > 1024) return BSA_ERR_UNSUPPORTED;   // one pairing thread per head of a segment
+  const int64_t seg = (int64_t)(Hq / Hkv) * nQB;
+  const int64_t grid = (int64_t)B * Hkv * ((seg + W - 1) / W);
+  hipLaunchKernelGGL(schedule_pairs_kernel, dim3((unsigned)grid), dim3(1024), 0, bsa_hip_stream(stream), row_ptr,
+                     col, lw, Hq, Hkv, nQB, W, wave_rows ? 0 : 1, n_xcd, R, row_perm, order, order2);
   BSA_LAUNCH_CHECK();
   return BSA_OK;
 }

@@ -90,6 +90,19 @@ class StepResult:
     stage1_decision: Optional[torch.Tensor] = None   # device int32 [1] (adaptive skip)
     stage1_stats: Optional[torch.Tensor] = None      # device float64 [7]
     kv_share: bool = False                            # query-head pairs served in one launch
+    order2: Optional[torch.Tensor] = None             # second rows of paired launch entries
+
+
+def _schedule(dw: DeviceWorkload, row_ptr, col, lw, wave_rows: int, n_xcd: int, row_perm, share: bool,
+              pairs: bool, stream):
+    """Launch tables (order, order2): with ``pairs`` the consecutive query
+    blocks of a head with identical lists share an entry (order2 holds the
+    second rows), else one row per entry (order2 None)."""
+    if pairs:
+        return api.schedule_pairs(row_ptr, col, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, lw=lw,
+                                  row_perm=row_perm, stream=stream)
+    return api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream, row_perm=row_perm,
+                        head_step=2 if share else 1, col=col), None
 
 
 def _stage1_order(dw: DeviceWorkload, row_ptr, col, stage1: str, iters: int, stream):
@@ -136,7 +149,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             fuse_scatter: bool = True, want_lse: bool = False, attn_events=None,
             v_dim_major: bool = True, stream=None, stage1: str = "auto", stage1_iters: int = 10,
             crm: bool = False, sampler: Optional[dict] = None, fuse_gather: bool = True,
-            overlap: bool = False, kv_share="auto") -> StepResult:
+            overlap: bool = False, kv_share="auto", pair_rows: bool = True) -> StepResult:
     """Run every step of the path once.  ``attn_events`` (start, end) are
     recorded around the attention launch on the same stream.  ``stage1``
     selects WaveAlign's stage 1 in front of the schedule: "auto" (the
@@ -155,14 +168,17 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     the workload's mask.  ``kv_share`` (True, False or "auto"): serve the
     identical rows of query-head pairs sharing a KV head in one launch (K/V
     tiles staged once for both heads); "auto" checks the rows on the device
-    and uses it where they are identical and the shape allows it."""
+    and uses it where they are identical and the shape allows it.  With
+    ``pair_rows`` (and no kv_share, CSR lists, dim-major V, 128-key blocks)
+    the schedule pairs consecutive query blocks of a head whose lists are
+    identical, and one launch entry serves both rows."""
     crm_rows = None
     if sampler is not None:
         return _forward_sampled(dw, sampler, schedule, n_xcd, wave_rows, fuse_scatter, want_lse, attn_events,
-                                stream, stage1, stage1_iters)
+                                stream, stage1, stage1_iters, pair_rows)
     if overlap and not crm:
         return _forward_overlapped(dw, schedule, n_xcd, wave_rows, fuse_scatter, fuse_gather, want_lse,
-                                   attn_events, v_dim_major, stream, stage1, stage1_iters, kv_share)
+                                   attn_events, v_dim_major, stream, stage1, stage1_iters, kv_share, pair_rows)
     if crm:
         if dw.lw_map is not None or not v_dim_major:
             raise ValueError("CRM lists carry no log-weights and need dim-major V")
@@ -193,9 +209,10 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
         elif not crm:
             row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
     share = False if crm else _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, stream)
+    order2 = None
     if schedule:
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
-                             row_perm=row_perm, head_step=2 if share else 1, col=col)
+        pairs = pair_rows and not share and not crm and v_dim_major and dw.block == 128
+        order, order2 = _schedule(dw, row_ptr, col, lw, wave_rows, n_xcd, row_perm, share, pairs, stream)
     sperm = perm_q if (dw.permuted and fuse_scatter) else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
@@ -203,7 +220,7 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
     gperm = perm_q if (dw.permuted and fuse_gather) else None
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
                             want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major, crm=crm_rows,
-                            gather_perm_q=gperm, kv_share=share, stream=stream)
+                            gather_perm_q=gperm, kv_share=share, order2=order2, stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if dw.permuted and not fuse_scatter:
@@ -212,12 +229,12 @@ def forward(dw: DeviceWorkload, schedule: bool = True, n_xcd: int = 8, wave_rows
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows, dec, stats, share)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, crm_rows, dec, stats, share, order2)
 
 
 def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: int, wave_rows: int,
                      fuse_scatter: bool, want_lse: bool, attn_events, stream, stage1: str,
-                     stage1_iters: int) -> StepResult:
+                     stage1_iters: int, pair_rows: bool = True) -> StepResult:
     """labels -> perms; Q/K gathered, V gathered and transposed; query-group
     and tile centroids; importance-sampled mask and log-weights -> CSR;
     schedule; attention with fused scatter-back."""
@@ -234,17 +251,17 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
     mask, lw_map, _ = api.is_sample(qbar, kbar, q_seg, sampler["uoff"], dw.B, dw.Hq, dw.Hkv, dw.N, dw.block,
                                     sampler["m_exact"], sampler["m_sample"], stream=stream)
     row_ptr, col, lw = api.build_csr(mask, None, 0.0, lw_map, dw.nQB, True, stream=stream)
-    order = dec = stats = None
+    order = order2 = dec = stats = None
     if schedule:
         row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, stream)
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=stream,
-                             row_perm=row_perm, col=col)
+        order, order2 = _schedule(dw, row_ptr, col, lw, wave_rows, n_xcd, row_perm, False,
+                                  pair_rows and dw.block == 128, stream)
     sperm = perm_q if fuse_scatter else None
     s = stream if stream is not None else torch.cuda.current_stream()
     if attn_events is not None:
         attn_events[0].record(s)
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
-                            want_lse=want_lse, causal=dw.causal, v_dim_major=True, stream=stream)
+                            want_lse=want_lse, causal=dw.causal, v_dim_major=True, order2=order2, stream=stream)
     if attn_events is not None:
         attn_events[1].record(s)
     if not fuse_scatter:
@@ -253,12 +270,12 @@ def _forward_sampled(dw: DeviceWorkload, sampler: dict, schedule: bool, n_xcd: i
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats, False, order2)
 
 
 def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_rows: int, fuse_scatter: bool,
                         fuse_gather: bool, want_lse: bool, attn_events, v_dim_major: bool, stream, stage1: str,
-                        stage1_iters: int, kv_share="auto") -> StepResult:
+                        stage1_iters: int, kv_share="auto", pair_rows: bool = True) -> StepResult:
     """The same step with two streams: [key labels -> perm_k, K gather, V
     gather + transpose] on a side stream beside [query labels -> perm_q,
     mask -> CSR without a host round trip, schedule] on the caller's stream;
@@ -290,9 +307,10 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
     if schedule:
         row_perm, dec, stats = _stage1_order(dw, row_ptr, col, stage1, stage1_iters, main)
     share = _kv_share(dw, kv_share, row_ptr, col, lw, v_dim_major, main)
+    order2 = None
     if schedule:
-        order = api.schedule(row_ptr, dw.B, dw.Hq, dw.Hkv, dw.nQB, wave_rows, n_xcd, stream=main,
-                             row_perm=row_perm, head_step=2 if share else 1, col=col)
+        pairs = pair_rows and not share and v_dim_major and dw.block == 128
+        order, order2 = _schedule(dw, row_ptr, col, lw, wave_rows, n_xcd, row_perm, share, pairs, main)
     main.wait_stream(side)
     for t in (perm_k, k, v):
         if t is not None:
@@ -303,7 +321,7 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
         attn_events[0].record(main)
     out, lse = api.attn_fwd(q, k, v, row_ptr, col, dw.block, lw=lw, order=order, scatter_perm_q=sperm,
                             want_lse=want_lse, causal=dw.causal, v_dim_major=v_dim_major,
-                            gather_perm_q=gperm, kv_share=share, stream=main)
+                            gather_perm_q=gperm, kv_share=share, order2=order2, stream=main)
     if attn_events is not None:
         attn_events[1].record(main)
     if dw.permuted and not fuse_scatter:
@@ -312,4 +330,4 @@ def _forward_overlapped(dw: DeviceWorkload, schedule: bool, n_xcd: int, wave_row
             inv = torch.empty_like(lse)
             inv.scatter_(1, perm_q.long(), lse)
             lse = inv
-    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats, share)
+    return StepResult(out, lse, row_ptr, col, lw, order, perm_q, perm_k, None, dec, stats, share, order2)

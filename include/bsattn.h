@@ -366,6 +366,36 @@ int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t B, int32_t 
                  bsa_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Row schedule with identical rows paired (launch tables for bsa_attn_fwd's
+ * order and order2).
+ * Source: the buckets, their longest-first order and the XCD deal of
+ * bsa_schedule (WaveAlign, section IV-D; head step 1); the pairing is the
+ * library's reading of the schedule's purpose (WaveAlign, section IV: rows
+ * that run together should reuse the same K/V blocks): two rows that list the
+ * same blocks are served by one launch entry, which stages each K/V tile once
+ * for both.  Within each bucket, walking its positions in ascending order, a
+ * position that is not already the second row of a pair is paired with the
+ * same head's next position (the next query block, or the next one of the
+ * stage-1 order) when that position lies in the bucket and both rows list
+ * the same blocks in the same order with the same log-weight bits (lw
+ * optional).  Entries are keyed by their tile count (nnz, or 2 nnz for a
+ * pair) and ordered as bsa_schedule orders rows (wave_rows 0: the sorted or
+ * the position order per bucket by the same signature cost, taken over each
+ * entry's first row); the second rows of pairs follow at the end of their
+ * bucket as empty entries.  order[i] receives entry i's first row (-1 for an
+ * empty entry), order2[i] its second row or -1.  row_ptr: device int32
+ * [B*Hq*nQB + 1]; col, lw: device, as bsa_csr_fill writes them (col
+ * required); row_perm: as bsa_schedule; order, order2: device int32
+ * [B*Hq*nQB] (outputs; every row appears exactly once in them).
+ * BSA_ERR_ARG for NULL pointers, non-positive sizes, Hq % Hkv != 0 or bad
+ * wave_rows / n_xcd; BSA_ERR_UNSUPPORTED for wave_rows > 2048, Hq / Hkv >
+ * 1024 or B*Hq*nQB >= 2^31.  Asynchronous.
+ * ------------------------------------------------------------------------- */
+int bsa_schedule_pairs(const int32_t *row_ptr, const int32_t *col, const float *lw, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t nQB, int32_t wave_rows, int32_t n_xcd, const int32_t *row_perm,
+                       int32_t *order, int32_t *order2, bsa_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Block-sparse attention forward.
  *
  * Source: InstaGen, section 3.1 Eq. (1)-(3) (l_ij = q_i . k_j / sqrt(d),
@@ -416,6 +446,18 @@ int bsa_schedule(const int32_t *row_ptr, const int32_t *col, int32_t B, int32_t 
  * compute nothing), n_order <= R / 2, and without order launch i serves the
  * i-th row of an even head.  Results equal those of kv_share = 0 on rows
  * that meet the precondition.
+ * order2 (optional, int32 [n_order], with order): launch entry i also serves
+ * row order2[i] when that is in [0, R), together with row order[i], staging
+ * each K/V tile once for both.  Such a pair must list the same blocks in the
+ * same order with the same log-weights (bit for bit) and lie in the same
+ * batch and KV-head group (e.g. adjacent query blocks of one cluster of a
+ * permuted head, which list identical blocks); bsa_schedule_pairs builds
+ * such tables.  Entries with order2[i] outside [0, R) serve row order[i]
+ * alone.  Requires kv_share = 0, v_layout = BSA_V_DIM_MAJOR, block = 128
+ * and crm = NULL (else BSA_ERR_UNSUPPORTED); BSA_ERR_ARG without order.
+ * Results equal those of the one-row launches within rounding (the pair
+ * accumulates all of a row's keys in one softmax state, the single row in
+ * two key halves merged at the end).
  * Asynchronous.
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -436,6 +478,7 @@ typedef struct {
   const uint32_t *crm; /* CRM rows in place of row_ptr/col, or NULL */
   const int32_t *gather_perm_q; /* query gather (int32 [B*Hq][N]), or NULL */
   int32_t kv_share; /* 0, or 2: rows of heads 2j and 2j + 1 of a KV group are identical */
+  const int32_t *order2; /* second row of each launch entry (identical pair), or NULL */
 } bsa_attn_args;
 
 int bsa_attn_fwd(const bsa_attn_args *a, bsa_stream_t stream);

@@ -91,6 +91,20 @@ def test_schedule_argument_errors(L):
     assert L.bsa_schedule(FAKE, None, 1, 6, 2, 8, 16, 8, None, 2, FAKE, None) == _lib.BSA_ERR_ARG   # G = 3
 
 
+def test_schedule_pairs_argument_errors(L):
+    f = L.bsa_schedule_pairs
+    ok = [FAKE, FAKE, None, 1, 4, 4, 8, 0, 8, None, FAKE, FAKE, None]
+    for i, bad, code in [(0, None, _lib.BSA_ERR_ARG), (1, None, _lib.BSA_ERR_ARG), (10, None, _lib.BSA_ERR_ARG),
+                         (11, None, _lib.BSA_ERR_ARG), (3, 0, _lib.BSA_ERR_ARG), (4, 6, _lib.BSA_ERR_ARG),
+                         (7, -1, _lib.BSA_ERR_ARG), (8, 65, _lib.BSA_ERR_ARG), (7, 4096, _lib.BSA_ERR_UNSUPPORTED)]:
+        a = list(ok)
+        a[i] = bad
+        assert f(*a) == code, (i, bad)
+    a = list(ok)
+    a[4], a[5] = 2048, 1                                   # 2048 query heads per KV head
+    assert f(*a) == _lib.BSA_ERR_UNSUPPORTED
+
+
 def test_pair_rows_equal_argument_errors(L):
     f = L.bsa_pair_rows_equal
     assert f(None, FAKE, None, 1, 4, 2, 8, FAKE, None) == _lib.BSA_ERR_ARG
@@ -288,6 +302,13 @@ def _args(**kw):
      _lib.BSA_ERR_UNSUPPORTED),
     (dict(kv_share=2, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), order=FAKE, n_order=17),
      _lib.BSA_ERR_ARG),                                                                      # > R / 2 launches
+    (dict(order2=FAKE, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024)),
+     _lib.BSA_ERR_ARG),                                                                      # order2 without order
+    (dict(order2=FAKE, order=FAKE), _lib.BSA_ERR_UNSUPPORTED),                                # token-major V
+    (dict(order2=FAKE, order=FAKE, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), block=64),
+     _lib.BSA_ERR_UNSUPPORTED),
+    (dict(order2=FAKE, order=FAKE, v_layout=1, v_str=_lib.I64x3(128 * 1024, 128 * 1024, 1024), kv_share=2),
+     _lib.BSA_ERR_UNSUPPORTED),
 ])
 def test_attn_argument_errors(L, kw, code):
     a = _args(**kw)

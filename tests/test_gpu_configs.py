@@ -51,8 +51,14 @@ def test_config_parity(name):
     # query-head pairs in one launch, from a head-step-2 schedule
     assert res.kv_share == (name == "llm_prefill")
     hs = 2 if res.kv_share else 1
-    assert np.array_equal(res.order.cpu().numpy(),
-                          oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8, head_step=hs, col=col))
+    if res.order2 is None:
+        assert np.array_equal(res.order.cpu().numpy(),
+                              oracle.schedule(rp, w.B, w.Hq, w.Hkv, w.nQB, W, 8, head_step=hs, col=col))
+    else:   # consecutive query blocks with identical lists paired in one launch entry
+        o1, o2 = oracle.schedule_pairs(rp, col, w.B, w.Hq, w.Hkv, w.nQB, W, 8, lw=lw)
+        assert np.array_equal(res.order.cpu().numpy(), o1)
+        assert np.array_equal(res.order2.cpu().numpy(), o2)
+        _log("  %d of %d launch entries serve a pair of rows" % (int((o2 >= 0).sum()), o2.size))
     _log("  integer steps bit-exact (nnz=%d)" % rp[-1])
     # stage-1 order of every head and the schedule built on it
     gp, ga = api.spectral_order(res.row_ptr, res.col, w.B * w.Hq, w.nQB, w.nQB, 10, want_angle=True)

@@ -97,7 +97,7 @@ CRM_CASES = {
 def test_crm_attention_matches_oracle_and_csr(name):
     w = synth.random_case(800 + list(CRM_CASES).index(name), **CRM_CASES[name])
     _log("case crm attention %s" % name)
-    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0)
+    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, pair_rows=False)
     _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, crm=True)
     assert torch.equal(r_crm.row_ptr, r_csr.row_ptr)
     # the CSR launch table may take the sequence order (the schedule sees the
@@ -122,7 +122,7 @@ def test_crm_long_rows_span_list_chunks(block, d, nblocks):
     1024-entry chunk at a time, from a position inside a word batch."""
     w = synth.random_case(900 + block, B=1, Hq=2, Hkv=1, N=block * nblocks - 37, d=d, block=block, density=0.97)
     _log("case crm long rows block=%d d=%d N=%d" % (block, d, w.N))
-    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0)
+    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, pair_rows=False)
     _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=0, crm=True)
     assert np.diff(r_crm.row_ptr.cpu().numpy()).max() > 1024
     assert torch.equal(r_crm.out, r_csr.out)
@@ -136,7 +136,7 @@ def test_crm_long_rows_span_list_chunks(block, d, nblocks):
 def test_crm_stage1_schedule_matches_csr():
     w = synth.random_case(950, B=1, Hq=2, Hkv=2, N=1500, d=128, block=128, density=0.3)
     _log("case crm stage-1 schedule")
-    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1="on", stage1_iters=6)
+    _, r_csr = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1="on", stage1_iters=6, pair_rows=False)
     _, r_crm = run_gpu(w, schedule=True, n_xcd=8, wave_rows=4, stage1="on", stage1_iters=6, crm=True)
     assert torch.equal(r_crm.order, r_csr.order)
     assert torch.equal(r_crm.out, r_csr.out)

@@ -79,17 +79,26 @@ def test_tiny_config_full():
 def test_order_invariance_and_determinism(vdm):
     w = make("b128_d128_perm_lw")
     _log("case determinism v_dim_major=%s" % vdm)
+    # one row per launch entry: every row is computed the same way whatever
+    # the launch order, so the outputs are bit-identical
     _, r1 = run_gpu(w, schedule=False, fuse_scatter=True, v_dim_major=vdm)
-    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True, v_dim_major=vdm)
-    _, r3 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, v_dim_major=vdm)
+    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True, v_dim_major=vdm, pair_rows=False)
+    _, r3 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, v_dim_major=vdm,
+                    pair_rows=False)
     _, r4 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, fuse_gather=False,
-                    v_dim_major=vdm)
+                    v_dim_major=vdm, pair_rows=False)
     a = r1.out.cpu().numpy()
     assert np.array_equal(a, r2.out.cpu().numpy())
     assert np.array_equal(a, r3.out.cpu().numpy())
     assert np.array_equal(a, r4.out.cpu().numpy())       # fused query gather == explicit gather
     assert np.array_equal(r1.lse.cpu().numpy(), r3.lse.cpu().numpy())
     assert np.array_equal(r1.lse.cpu().numpy(), r4.lse.cpu().numpy())
+    # paired launch entries (the default schedule): the same tables give the
+    # same bits, fused or explicit scatter
+    _, p1 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=True, v_dim_major=vdm)
+    _, p2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=5, fuse_scatter=False, v_dim_major=vdm)
+    assert (p1.order2 is not None) == vdm
+    assert torch.equal(p1.out, p2.out) and torch.equal(p1.lse, p2.lse)
 
 
 @pytest.mark.parametrize("name", ["b128_d128_perm_lw", "b64_d64_gqa_T", "b128_d128_causal_gqa"])
@@ -103,6 +112,9 @@ def test_overlapped_step_is_bit_identical(name):
     nnz = int(r1.row_ptr[-1].item())
     assert torch.equal(r1.row_ptr, r2.row_ptr) and torch.equal(r1.col, r2.col[:nnz])
     assert torch.equal(r1.order, r2.order)
+    assert (r1.order2 is None) == (r2.order2 is None)
+    if r1.order2 is not None:
+        assert torch.equal(r1.order2, r2.order2)
     assert torch.equal(r1.out, r2.out) and torch.equal(r1.lse, r2.lse)
 
 
@@ -315,8 +327,8 @@ def test_schedule_with_row_order_bit_exact():
 def test_stage1_schedule_leaves_outputs_unchanged():
     w = make("b128_d128_perm_lw")
     _log("case stage-1 schedule invariance")
-    _, r1 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16, stage1="off")
-    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16, stage1="on", stage1_iters=8)
+    _, r1 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16, stage1="off", pair_rows=False)
+    _, r2 = run_gpu(w, schedule=True, n_xcd=8, wave_rows=16, stage1="on", stage1_iters=8, pair_rows=False)
     assert not np.array_equal(r1.order.cpu().numpy(), r2.order.cpu().numpy())
     assert np.array_equal(r1.out.cpu().numpy(), r2.out.cpu().numpy())
     assert np.array_equal(r1.lse.cpu().numpy(), r2.lse.cpu().numpy())
